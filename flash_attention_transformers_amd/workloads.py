@@ -1,0 +1,153 @@
+"""Seeded synthetic attention inputs and the five workload shapes.
+
+This module holds no attention arithmetic: it only draws the inputs that both
+the HIP path and the CPU checker consume, so that the two always see the same
+values.
+
+Recipe (the same for every workload):
+
+* ``numpy.random.default_rng(seed)`` (PCG64), then ``standard_normal`` in
+  float32, drawn in the order q, k, v, dO, each with its full BHSD shape.
+* Optional per-tensor multipliers (the DiT self-attention workload scales q
+  and k by float32(1/sqrt(2)) *before* rounding).
+* For bf16 workloads every tensor is rounded to bfloat16 with
+  round-to-nearest-even; the checker receives exactly those rounded values
+  upcast to float64, so input rounding is never counted as kernel error.
+
+The shapes follow the decoder-training and DiT/world-model workloads of the
+source pages: the LingBot pipeline report ("Attention: real inputs, backends,
+error and timing" and the FA2/FA3 hardware-comparison sections: head dim 128,
+a per-GPU share of 10 heads, 30x52 latent tokens per frame, text KV of 512)
+and the xtrain evolution page (table row T14: head dim 64 decoder; row T15:
+grouped KV heads).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    Skv: int
+    D: int
+    causal: bool
+    dtype: str  # "bf16" or "f32"
+    seed: int
+    backward: bool
+    qk_mult: float = 1.0  # multiplier applied to q and k before rounding
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    def fwd_flop(self) -> float:
+        """Credited forward work: 4*B*Hq*Sq*Skv*D, halved when causal."""
+        f = 4.0 * self.B * self.Hq * self.Sq * self.Skv * self.D
+        return f / 2 if self.causal else f
+
+    def bwd_flop(self) -> float:
+        """Credited backward work: 2.5x the credited forward work."""
+        return 2.5 * self.fwd_flop()
+
+    def with_shape(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    w.name: w
+    for w in [
+        Workload("tiny_mha_f32", 1, 2, 2, 128, 128, 64, False, "f32", 1, True),
+        Workload("decoder_mha_causal", 8, 12, 12, 1024, 1024, 64, True, "bf16", 2, True),
+        Workload("gqa_causal", 4, 32, 8, 4096, 4096, 128, True, "bf16", 3, True),
+        Workload("dit_self", 1, 10, 10, 32760, 32760, 128, False, "bf16", 4, False,
+                 qk_mult=1.0 / math.sqrt(2.0)),
+        Workload("dit_cross_512", 1, 10, 10, 32760, 512, 128, False, "bf16", 51, True),
+        Workload("dit_cross_257", 1, 10, 10, 32760, 257, 128, False, "bf16", 52, True),
+    ]
+}
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    Inputs here are finite normal draws; NaN/Inf are not produced by the
+    generator and are not handled specially.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> 16) & 1
+    rounded = (bits + 0x7FFF + lsb) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host copies of one seeded input set.
+
+    ``vals`` holds float32 arrays with exactly the values the GPU sees (for
+    bf16 workloads these are the rounded values); ``bits`` holds the raw
+    bf16 bit patterns (uint16) for bf16 workloads, else None.
+    """
+    workload: Workload
+    vals: Dict[str, np.ndarray]
+    bits: Optional[Dict[str, np.ndarray]]
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> Inputs:
+    rng = np.random.default_rng(w.seed if seed is None else seed)
+    shapes = {
+        "q": (w.B, w.Hq, w.Sq, w.D),
+        "k": (w.B, w.Hkv, w.Skv, w.D),
+        "v": (w.B, w.Hkv, w.Skv, w.D),
+        "do": (w.B, w.Hq, w.Sq, w.D),
+    }
+    raw = {}
+    for name in ("q", "k", "v", "do"):
+        a = rng.standard_normal(shapes[name], dtype=np.float32)
+        if name in ("q", "k") and w.qk_mult != 1.0:
+            a = a * np.float32(w.qk_mult)
+        raw[name] = a
+    if w.dtype == "bf16":
+        bits = {n: round_to_bf16_bits(a) for n, a in raw.items()}
+        vals = {n: bf16_bits_to_f32(b) for n, b in bits.items()}
+        return Inputs(w, vals, bits)
+    return Inputs(w, raw, None)
+
+
+def to_torch(inp: Inputs, device) -> Dict[str, "object"]:
+    """Device tensors (torch) holding exactly ``inp``'s values."""
+    import torch
+
+    out = {}
+    for n, a in inp.vals.items():
+        if inp.bits is not None:
+            t = torch.from_numpy(inp.bits[n].view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(a)
+        out[n] = t.to(device).contiguous()
+    return out
+
+
+def head_sample(w: Workload, n: int, seed: int = 0) -> Tuple[Tuple[int, int], ...]:
+    """A fixed, seeded choice of (b, h) pairs, always including the first and
+    the last head."""
+    pairs = [(0, 0), (w.B - 1, w.Hq - 1)]
+    rng = np.random.default_rng(1000 + seed)
+    while len(pairs) < min(n, w.B * w.Hq):
+        p = (int(rng.integers(w.B)), int(rng.integers(w.Hq)))
+        if p not in pairs:
+            pairs.append(p)
+    return tuple(pairs)
