@@ -1,0 +1,209 @@
+"""Benchmark of the fused attention hot path on one MI355X.
+
+One step = mattn_fwd + mattn_bwd (forward kernel, D = sum(dO*O) preprocess,
+dK/dV kernel, dQ kernel) over one batch of seeded synthetic input that is
+already resident in HBM.  Default workload: GQA causal training attention,
+B=4, Hq=32, Hkv=8, S=4096, D=128, bf16 (the long-sequence configuration that
+exercises every step of the path, including the grouped-KV head map and the
+group-summed backward).
+
+Prints ONE JSON line.  `value` is credited TFLOP/s of the whole step:
+(4*B*Hq*Sq*Skv*D forward + 2.5x that backward, halved for causal) / step time.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix / packed vector peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def _traffic_from_profile(workload: str):
+    """Per-launch HBM bytes of the forward kernel from the committed rocprofv3
+    counter summary, or None if absent or if the kernel source changed since
+    the counters were taken."""
+    path = os.path.join(PROFILES, f"fwd_bf16_kernel_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
+    m_b = re.search(r"HBM bytes per launch \(calibrated\): ([0-9.eE+]+)", text)
+    src = os.path.join(ROOT, "flash_attention_transformers_amd", "csrc", "fwd_bf16.hip")
+    if not m_sha or not m_b or m_sha.group(1) != _sha(src):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(w, budget_s: float = 12.0):
+    """Time the float64 oracle on the host cores on a bounded sample of the
+    same workload: whole KV-head groups (all their query heads), forward and
+    backward, until the time budget is spent.  Rate = credited FLOP of the
+    sample / time."""
+    import numpy as np
+
+    import oracle
+    from flash_attention_transformers_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    G = w.Hq // w.Hkv
+    small = w.with_shape(B=1, Hq=G, Hkv=1)  # one KV-head group at full sequence length
+    inp = W.make_inputs(small, seed=w.seed)
+    v = inp.vals
+    groups = 0
+    t0 = time.perf_counter()
+    while True:
+        for r in range(G):
+            q, k, vv, do = v["q"][0, r], v["k"][0, 0], v["v"][0, 0], v["do"][0, r]
+            oracle.forward_head(q, k, vv, w.causal, w.scale)
+            if w.backward:
+                oracle.backward_head(q, k, vv, do, w.causal, w.scale)
+        groups += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or groups >= w.B * w.Hkv:
+            break
+    flop_per_group = small.fwd_flop() * (3.5 if w.backward else 1.0)
+    return {
+        "value": groups * flop_per_group / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{groups} of {w.B * w.Hkv} (batch, kv-head) groups, each with its {G} query "
+                  f"head(s) at Sq={w.Sq}, Skv={w.Skv}, D={w.D}, causal={w.causal}, "
+                  f"{'forward+backward' if w.backward else 'forward'}, float64, "
+                  f"{el:.1f} s; rate credited like the GPU (causal halved)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa_causal")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(attention heads shard across GPUs with no change to the kernel).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import flash_attention_transformers_amd as fa
+    from flash_attention_transformers_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    fa.load_library()
+    inp = W.make_inputs(w)
+    t = W.to_torch(inp, dev)
+    del inp
+    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = fa.bwd_workspace(q, k)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fa.mattn_fwd(q, k, v, o, lse, w.causal, w.scale, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if w.backward:
+            fa.mattn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.causal, w.scale, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if w.backward else 0.0
+
+    fwd_flop = w.fwd_flop()
+    step_flop = fwd_flop + (w.bwd_flop() if w.backward else 0.0)
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+    value = step_flop / (ms_step * 1e-3) / 1e12
+    fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
+    bwd_tf = w.bwd_flop() / (bwd_ms * 1e-3) / 1e12 if w.backward else None
+
+    line = {
+        "metric": "attention TFLOPS fwd and fwd+bwd at 1 MI355X; % of bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1), resident in HBM)",
+        "config": {
+            "workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Sq={w.Sq} Skv={w.Skv} "
+                        f"D={w.D} causal={int(w.causal)}; step = forward + backward",
+            "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * value / peak, 2),
+        "fwd_tflops": round(fwd_tf, 2),
+        "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
+        "bwd_tflops": None if bwd_tf is None else round(bwd_tf, 2),
+        "bwd_pct_of_peak": None if bwd_tf is None else round(100 * bwd_tf / peak, 2),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {
+            "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
+            "bound": "mfma",
+            "achieved": round(fwd_tf, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tf / peak, 4),
+            "traffic": _traffic_from_profile(w.name),
+        },
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

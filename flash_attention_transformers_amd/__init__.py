@@ -1,0 +1,171 @@
+"""libmattn: fused scaled-dot-product attention for MI355X (gfx950).
+
+Thin ctypes binding over the C ABI declared in include/mattn.h.  Every step
+of the computation runs in the HIP kernels of libmattn.so; this module only
+marshals arguments.  PyTorch supplies device memory and the current stream.
+
+    o, lse = fwd(q, k, v, causal=False, scale=None)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
+
+The ``mattn_*`` functions mirror the C entry points one to one and take
+pre-allocated tensors.  There is no fallback: if libmattn.so is missing or
+fails to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmattn.so")
+
+MATTN_OK, MATTN_ERR_INVALID_ARG, MATTN_ERR_UNSUPPORTED, MATTN_ERR_LAUNCH = 0, 1, 2, 3
+MATTN_BF16, MATTN_F32 = 0, 1
+
+_lib = None
+
+
+class MattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libmattn: {msg} (status {status})")
+        self.status = status
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libmattn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.mattn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    lib.mattn_fwd.restype = i
+    lib.mattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i,
+                              vp, sz, vp]
+    lib.mattn_bwd.restype = i
+    lib.mattn_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.mattn_bwd_workspace_size.restype = sz
+    lib.mattn_strerror.argtypes = [i]
+    lib.mattn_strerror.restype = ctypes.c_char_p
+    lib.mattn_version.argtypes = []
+    lib.mattn_version.restype = i
+    _lib = lib
+    return lib
+
+
+def mattn_strerror(status: int) -> str:
+    return load_library().mattn_strerror(status).decode()
+
+
+def mattn_version() -> int:
+    return load_library().mattn_version()
+
+
+def mattn_bwd_workspace_size(B: int, Hq: int, Hkv: int, Sq: int, Skv: int, D: int) -> int:
+    return load_library().mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D)
+
+
+def _check(status: int):
+    if status != MATTN_OK:
+        raise MattnError(status, mattn_strerror(status))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return MATTN_BF16
+    if t.dtype == torch.float32:
+        return MATTN_F32
+    raise TypeError(f"libmattn supports bfloat16 and float32, got {t.dtype}")
+
+
+def _stream_handle(t, stream) -> int:
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _shapes(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D] tensors")
+    B, Hq, Sq, D = q.shape
+    _, Hkv, Skv, _ = k.shape
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+def _require(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("libmattn tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("libmattn tensors must be contiguous (BHSD row-major)")
+
+
+def mattn_fwd(q, k, v, o, lse, causal: bool = False, scale: Optional[float] = None,
+              stream=None) -> None:
+    """Forward into pre-allocated o [B,Hq,Sq,D] and lse [B,Hq,Sq] (float32)."""
+    _require(q, k, v, o, lse)
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = load_library().mattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, Hq, Hkv, Sq, Skv, D, int(causal),
+                                  float(scale), _dtype_code(q), _stream_handle(q, stream))
+    _check(st)
+
+
+def mattn_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,
+              scale: Optional[float] = None, stream=None) -> None:
+    """Backward into pre-allocated dq, dk, dv; `workspace` is a uint8 device
+    tensor of at least mattn_bwd_workspace_size() bytes."""
+    _require(q, k, v, o, lse, do, dq, dk, dv, workspace)
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().mattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D, int(causal),
+                                  float(scale), _dtype_code(q), workspace.data_ptr(), nbytes,
+                                  _stream_handle(q, stream))
+    _check(st)
+
+
+def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, stream=None):
+    """Allocate and return (o, lse)."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    mattn_fwd(q, k, v, o, lse, causal, scale, stream)
+    return o, lse
+
+
+def bwd_workspace(q, k):
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
+    n = mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=q.device)
+
+
+def bwd(q, k, v, o, lse, do, causal: bool = False, scale: Optional[float] = None,
+        workspace=None, stream=None) -> Tuple[object, object, object]:
+    """Allocate and return (dq, dk, dv)."""
+    import torch
+
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    if workspace is None:
+        workspace = bwd_workspace(q, k)
+    mattn_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, causal, scale, stream)
+    return dq, dk, dv

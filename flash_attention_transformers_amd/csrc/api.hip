@@ -1,0 +1,132 @@
+// C-ABI entry points of libmattn: argument validation and kernel dispatch.
+// Every check happens before anything is enqueued; on error nothing runs and
+// no output is touched.
+#include <math.h>
+#include <stdint.h>
+
+#include <initializer_list>
+
+#include "mattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr long long kMaxElems = 1LL << 31;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Sizes {
+  long long q_elems, kv_elems, rows;
+};
+
+// Size, flag and scale validation shared by forward and backward.
+mattn_status check_args(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                        mattn_dtype dtype, Sizes* out) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || Skv < 0 || D < 0) return MATTN_ERR_INVALID_ARG;
+  if (Hkv == 0 || Hq % Hkv != 0) return MATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return MATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return MATTN_ERR_INVALID_ARG;
+  if (dtype != MATTN_BF16 && dtype != MATTN_F32) return MATTN_ERR_INVALID_ARG;
+  const long long rows = (long long)B * Hq * Sq;
+  const long long kv_rows = (long long)B * Hkv * Skv;
+  if (rows > 0 && Skv == 0) return MATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return MATTN_ERR_UNSUPPORTED;
+  if (rows * D >= kMaxElems || kv_rows * D >= kMaxElems) return MATTN_ERR_UNSUPPORTED;
+  if (causal && Sq > Skv) return MATTN_ERR_UNSUPPORTED;
+  out->q_elems = rows * D;
+  out->kv_elems = kv_rows * D;
+  out->rows = rows;
+  return MATTN_OK;
+}
+
+// Every pointer in the list must be non-null and 16-byte aligned.
+bool ptrs_ok(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t dlt_bytes(int B, int Hq, int Sq) { return round256((size_t)B * Hq * Sq * sizeof(float)); }
+
+size_t part_bytes(int B, int Hkv, int Sq, int Skv, int D) {
+  const int ns = mattn::bwd_nsplit(B, Hkv, Sq, Skv);
+  if (ns <= 1) return 0;
+  const size_t n_kt = (size_t)(Skv + mattn::BWD_BN - 1) / mattn::BWD_BN;
+  return round256(2 * (size_t)ns * B * Hkv * n_kt * mattn::BWD_BN * D * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" {
+
+mattn_status mattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                       mattn_dtype dtype, hipStream_t stream) {
+  Sizes sz;
+  mattn_status st = check_args(B, Hq, Hkv, Sq, Skv, D, causal, scale, dtype, &sz);
+  if (st != MATTN_OK) return st;
+  if (sz.rows == 0) return MATTN_OK;
+  if (!ptrs_ok({q, k, v, o, lse})) return MATTN_ERR_INVALID_ARG;
+  const mattn::Problem p{B, Hq, Hkv, Sq, Skv, D, causal, scale};
+  hipError_t e = dtype == MATTN_BF16
+                     ? mattn::launch_fwd_bf16(p, q, k, v, o, lse, stream)
+                     : mattn::launch_fwd_f32(p, (const float*)q, (const float*)k,
+                                             (const float*)v, (float*)o, lse, stream);
+  return e == hipSuccess ? MATTN_OK : MATTN_ERR_LAUNCH;
+}
+
+size_t mattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0 || Hq % Hkv != 0) return 0;
+  if (D != 64 && D != 128) return 0;
+  return dlt_bytes(B, Hq, Sq) + part_bytes(B, Hkv, Sq, Skv, D);
+}
+
+mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                       int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                       mattn_dtype dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  Sizes sz;
+  mattn_status st = check_args(B, Hq, Hkv, Sq, Skv, D, causal, scale, dtype, &sz);
+  if (st != MATTN_OK) return st;
+  if (sz.kv_elems > 0 && !ptrs_ok({dk, dv})) return MATTN_ERR_INVALID_ARG;
+  if (sz.rows > 0) {
+    if (!ptrs_ok({q, k, v, o, lse, dout, dq, workspace})) return MATTN_ERR_INVALID_ARG;
+    if (workspace_bytes < mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D))
+      return MATTN_ERR_INVALID_ARG;
+  }
+  if (sz.rows == 0) {
+    // No query rows: every key receives a zero gradient.
+    const size_t words = (size_t)sz.kv_elems * (dtype == MATTN_BF16 ? 2 : 4) / 4;
+    if (mattn::launch_zero_words(dk, words, stream) != hipSuccess) return MATTN_ERR_LAUNCH;
+    if (mattn::launch_zero_words(dv, words, stream) != hipSuccess) return MATTN_ERR_LAUNCH;
+    return MATTN_OK;
+  }
+  const mattn::Problem p{B, Hq, Hkv, Sq, Skv, D, causal, scale};
+  float* dlt = (float*)workspace;
+  float* part = (float*)((char*)workspace + dlt_bytes(B, Hq, Sq));
+  hipError_t e = mattn::launch_bwd_preprocess(p, dtype == MATTN_BF16, o, dout, dlt, stream);
+  if (e != hipSuccess) return MATTN_ERR_LAUNCH;
+  if (dtype == MATTN_BF16)
+    e = mattn::launch_bwd_bf16(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream);
+  else
+    e = mattn::launch_bwd_f32(p, (const float*)q, (const float*)k, (const float*)v, lse, dlt,
+                              (const float*)dout, (float*)dq, (float*)dk, (float*)dv, stream);
+  return e == hipSuccess ? MATTN_OK : MATTN_ERR_LAUNCH;
+}
+
+const char* mattn_strerror(mattn_status s) {
+  switch (s) {
+    case MATTN_OK: return "success";
+    case MATTN_ERR_INVALID_ARG: return "invalid argument";
+    case MATTN_ERR_UNSUPPORTED: return "unsupported problem (head dim, size or causal Sq > Skv)";
+    case MATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int mattn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,516 @@
+// Flash-style attention backward, bf16 I/O, fp32 statistics and accumulation.
+//
+// The method is the backward of the xtrain evolution page's fused kernel
+// (infrastructure-phase table, row T14): the scores are recomputed from Q, K
+// and the saved log-sum-exp, and the per-row scalar D = sum(dO * O)
+// simplifies the softmax Jacobian to dS = P * (dP - D).  Grouped KV heads
+// follow row T15: each KV head's dK/dV is the sum over its G query heads,
+// done here in registers in ascending group order, with no atomics, so the
+// result is bitwise reproducible.
+//
+// Three kernels on one stream:
+//  1. preprocess: Dlt[row] = sum_d dO[row,d] * O[row,d]            (HBM bound)
+//  2. dK/dV: one workgroup per 128 keys of one KV head; each wave keeps its
+//     32 keys' K and V rows in registers as MFMA B operands and walks the
+//     query tiles of every query head of the group:
+//        S = Q K^T, dP = dO V^T            (lane = key column)
+//        P = 2^(S*scale*log2e - LSE*log2e), dS = P (dP - Dlt)
+//        dV^T += dO^T P,  dK^T += Q^T dS   (P, dS fed from registers)
+//     Shapes with few KV tiles (short cross-attention KV) split the query
+//     range into fixed chunks that write fp32 partials, summed afterwards in
+//     chunk order by a reduction kernel.
+//  3. dQ: one workgroup per 128 query rows; each wave keeps its 32 rows of Q
+//     and dO in registers and walks the K/V tiles:
+//        S^T = K Q^T, dP^T = V dO^T        (lane = query column)
+//        dQ^T += K^T dS^T
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mattn {
+
+int bwd_nsplit(int B, int Hkv, int Sq, int Skv) {
+  if (B <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0) return 1;
+  const long long n_kt = (Skv + BWD_BN - 1) / BWD_BN;
+  const long long wgs = (long long)B * Hkv * n_kt;
+  const long long target = 512;
+  if (wgs >= target) return 1;
+  const long long n_qt = (Sq + BWD_BMQ - 1) / BWD_BMQ;
+  long long ns = (target + wgs - 1) / wgs;
+  const long long cap = n_qt / 8;  // keep at least 8 query tiles per chunk
+  if (ns > cap) ns = cap;
+  return ns < 1 ? 1 : (int)ns;
+}
+
+namespace {
+
+constexpr int THREADS = 256;
+
+// ----------------------------------------------------------------------------
+// 1. preprocess
+template <typename T, int D>
+__global__ __launch_bounds__(THREADS)
+void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ dlt,
+                    long long rows) {
+  constexpr int TPR = D / 8;  // threads per row, 8 elements each
+  constexpr int RPB = THREADS / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = threadIdx.x % TPR;
+  float s = 0.f;
+  if (row < rows) {
+    const T* po = O + row * D + c * 8;
+    const T* pd = dO + row * D + c * 8;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s += (float)pd[e] * (float)po[e];
+  }
+#pragma unroll
+  for (int o = TPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+  if (c == 0 && row < rows) dlt[row] = s;
+}
+
+// ----------------------------------------------------------------------------
+// Load 8 rows x 2 columns of a [rows x D] bf16 tile with 4-byte loads and
+// write it to LDS twice: row-major (pitch NP) and transposed with the swz row
+// order (pitch TP).  `pos0` is the first (multiple-of-8) transposed position;
+// the rows it covers are (pos & ~15) + swz(pos & 15).
+template <int D, int NP, int TP>
+struct DualTile {
+  uint32_t w[8];
+  __device__ __forceinline__ void load(const bf16* base, int row0, int nrows_valid, int pos0, int c2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = pos0 + e;
+      const int r = (pos & ~15) + swz(pos & 15);
+      w[e] = ld4(base + (size_t)(row0 + r) * D + 2 * c2, r < nrows_valid);
+    }
+  }
+  __device__ __forceinline__ void store(bf16* nat, bf16* tr, int pos0, int c2) const {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = pos0 + e;
+      const int r = (pos & ~15) + swz(pos & 15);
+      *reinterpret_cast<uint32_t*>(&nat[r * NP + 2 * c2]) = w[e];
+    }
+    uint4 lo, hi;
+    split_pairs(w, lo, hi);
+    *reinterpret_cast<uint4*>(&tr[(2 * c2) * TP + pos0]) = lo;
+    *reinterpret_cast<uint4*>(&tr[(2 * c2 + 1) * TP + pos0]) = hi;
+  }
+};
+
+// ----------------------------------------------------------------------------
+// 2. dK/dV
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(THREADS, 1)
+void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                     const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                     const float* __restrict__ LSE, const float* __restrict__ DLT,
+                     bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ part,
+                     int Hq, int G, int Sq, int Skv, float scale, float c, int n_kt,
+                     int nsplit, int q_chunk) {
+  constexpr int BMQ = BWD_BMQ;
+  constexpr int NP = D + 8;
+  constexpr int TP = BMQ + 8;
+  constexpr int LTPR = D / 2;             // loader threads per row pair-column set
+  constexpr int LGROUPS = BMQ / 8;        // 8-row groups per tile
+  constexpr int LTHREADS = LTPR * LGROUPS;
+  static_assert(LTHREADS <= THREADS, "tile loader needs more threads than the workgroup has");
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BMQ * NP];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[BMQ * NP];
+  __shared__ __attribute__((aligned(16))) bf16 Qt[D * TP];
+  __shared__ __attribute__((aligned(16))) bf16 dOt[D * TP];
+  __shared__ __attribute__((aligned(16))) float lse_s[BMQ];
+  __shared__ __attribute__((aligned(16))) float dlt_s[BMQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int Hkv = Hq / G;
+
+  const int split = blockIdx.x % nsplit;
+  const int rest = blockIdx.x / nsplit;
+  const int kt = rest % n_kt;
+  const int bkv = rest / n_kt;
+  const int b = bkv / Hkv, kvh = bkv % Hkv;
+  const int k0 = kt * BWD_BN;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+  const int diag = Skv - Sq;
+
+  const size_t kv_off = (size_t)bkv * Skv * D;
+  bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    kf[s] = as_bf16x8(ld16(K + kv_off + (size_t)key * D + 16 * s + 8 * g, key < Skv));
+    vf[s] = as_bf16x8(ld16(V + kv_off + (size_t)key * D + 16 * s + 8 * g, key < Skv));
+  }
+  f32x16 adk[D / 32], adv[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    adk[db] = zero_f32x16();
+    adv[db] = zero_f32x16();
+  }
+
+  // Query range of this chunk (q_chunk is a multiple of BMQ).
+  const int qs = split * q_chunk;
+  const int qe = min(Sq, qs + q_chunk);
+  int q_lo = qs;
+  if (CAUSAL) {
+    const int first = k0 - diag;  // first query that can see key k0
+    if (first > q_lo) q_lo = (first / BMQ) * BMQ;
+  }
+  const int nq = qe > q_lo ? (qe - q_lo + BMQ - 1) / BMQ : 0;
+  const int n_it = G * nq;
+
+  const bool loader = tid < LTHREADS;
+  const int c2 = tid % LTPR, pos0 = 8 * (tid / LTPR);
+  DualTile<D, NP, TP> tq, tdo;
+  float pre_lse = 0.f, pre_dlt = 0.f;
+
+  auto load_it = [&](int it) {
+    const int r = it / nq, qi = it % nq;
+    const int h = kvh * G + r;
+    const int qt0 = q_lo + qi * BMQ;
+    const size_t q_off = ((size_t)(b * Hq + h) * Sq + qt0) * D;
+    const int nvalid = Sq - qt0;
+    if (loader) {
+      tq.load(Q + q_off, 0, nvalid, pos0, c2);
+      tdo.load(dO + q_off, 0, nvalid, pos0, c2);
+    }
+    if (tid < BMQ) {
+      const int qq = qt0 + tid;
+      const size_t ro = (size_t)(b * Hq + h) * Sq + qq;
+      pre_lse = qq < Sq ? LSE[ro] * MATTN_LOG2E : MATTN_INF;
+      pre_dlt = qq < Sq ? DLT[ro] : 0.f;
+    }
+  };
+
+  if (n_it > 0) load_it(0);
+  for (int it = 0; it < n_it; ++it) {
+    const int qt0 = q_lo + (it % nq) * BMQ;
+    __syncthreads();
+    if (loader) {
+      tq.store(Qs, Qt, pos0, c2);
+      tdo.store(dOs, dOt, pos0, c2);
+    }
+    if (tid < BMQ) {
+      lse_s[tid] = pre_lse;
+      dlt_s[tid] = pre_dlt;
+    }
+    __syncthreads();
+    if (it + 1 < n_it) load_it(it + 1);
+
+    // S = Q K^T and dP = dO V^T: lane = key column, regs = query rows.
+    f32x16 s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[l32 * NP + 16 * st + 8 * g]);
+      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dOs[l32 * NP + 16 * st + 8 * g]);
+      s = mfma32(aq, kf[st], s);
+      dp = mfma32(ad, vf[st], dp);
+    }
+    const bool need_mask = CAUSAL && (kw0 + 31 > qt0 + diag);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const f32x4 L = *reinterpret_cast<const f32x4*>(&lse_s[8 * blk + 4 * g]);
+      const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[8 * blk + 4 * g]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * blk + j;
+        float p = fast_exp2(__builtin_fmaf(s[i], c, -L[j]));
+        if (need_mask && key > qt0 + crow(i, g) + diag) p = 0.f;
+        s[i] = p;
+        dp[i] = p * (dp[i] - Dl[j]);
+      }
+    }
+    bf16x8 pb[2], dsb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pb[t][e] = (bf16)s[8 * t + e];
+        dsb[t][e] = (bf16)dp[8 * t + e];
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS.
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 ado = *reinterpret_cast<const bf16x8*>(&dOt[(db * 32 + l32) * TP + 16 * t + 8 * g]);
+        const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(&Qt[(db * 32 + l32) * TP + 16 * t + 8 * g]);
+        adv[db] = mfma32(ado, pb[t], adv[db]);
+        adk[db] = mfma32(aqt, dsb[t], adk[db]);
+      }
+  }
+
+  if (key >= Skv) return;
+  if (nsplit == 1) {
+    bf16* pk = dK + kv_off + (size_t)key * D;
+    bf16* pv = dV + kv_off + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = db * 32 + r * 8 + g * 4;
+        uint2 wk, wv;
+        wk.x = pack_bf16x2(adk[db][4 * r] * scale, adk[db][4 * r + 1] * scale);
+        wk.y = pack_bf16x2(adk[db][4 * r + 2] * scale, adk[db][4 * r + 3] * scale);
+        wv.x = pack_bf16x2(adv[db][4 * r], adv[db][4 * r + 1]);
+        wv.y = pack_bf16x2(adv[db][4 * r + 2], adv[db][4 * r + 3]);
+        *reinterpret_cast<uint2*>(pk + d) = wk;
+        *reinterpret_cast<uint2*>(pv + d) = wv;
+      }
+  } else {
+    // fp32 partials: [2][nsplit][B*Hkv][n_kt*BWD_BN][D]
+    const size_t rows_all = (size_t)(gridDim.x / nsplit / n_kt) * n_kt * BWD_BN;
+    const size_t half = (size_t)nsplit * rows_all * D;
+    const size_t ro = ((size_t)split * rows_all + (size_t)bkv * n_kt * BWD_BN + key) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = db * 32 + r * 8 + g * 4;
+        *reinterpret_cast<f32x4*>(part + ro + d) =
+            f32x4{adk[db][4 * r], adk[db][4 * r + 1], adk[db][4 * r + 2], adk[db][4 * r + 3]};
+        *reinterpret_cast<f32x4*>(part + half + ro + d) =
+            f32x4{adv[db][4 * r], adv[db][4 * r + 1], adv[db][4 * r + 2], adv[db][4 * r + 3]};
+      }
+  }
+}
+
+// Sum of the split partials in fixed chunk order, scaled (dK) and rounded.
+__global__ __launch_bounds__(THREADS)
+void bwd_reduce_kernel(const float* __restrict__ part, bf16* __restrict__ dK,
+                       bf16* __restrict__ dV, int nsplit, int BKV, int Skv, int n_kt, int D,
+                       float scale) {
+  const long long total4 = (long long)BKV * Skv * D / 4;
+  const long long i4 = (long long)blockIdx.x * THREADS + threadIdx.x;
+  if (i4 >= total4) return;
+  const long long e = i4 * 4;
+  const long long row = e / D;  // bkv*Skv + key
+  const int d = (int)(e % D);
+  const long long bkv = row / Skv, key = row % Skv;
+  const size_t rows_all = (size_t)BKV * n_kt * BWD_BN;
+  const size_t half = (size_t)nsplit * rows_all * D;
+  const size_t src = ((size_t)bkv * n_kt * BWD_BN + key) * D + d;
+  f32x4 sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    sk += *reinterpret_cast<const f32x4*>(part + (size_t)s * rows_all * D + src);
+    sv += *reinterpret_cast<const f32x4*>(part + half + (size_t)s * rows_all * D + src);
+  }
+  uint2 wk, wv;
+  wk.x = pack_bf16x2(sk[0] * scale, sk[1] * scale);
+  wk.y = pack_bf16x2(sk[2] * scale, sk[3] * scale);
+  wv.x = pack_bf16x2(sv[0], sv[1]);
+  wv.y = pack_bf16x2(sv[2], sv[3]);
+  *reinterpret_cast<uint2*>(dK + e) = wk;
+  *reinterpret_cast<uint2*>(dV + e) = wv;
+}
+
+// ----------------------------------------------------------------------------
+// 3. dQ
+constexpr int DQ_BM = 128;
+constexpr int DQ_BN = 64;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(THREADS, (D == 128 ? 1 : 2))
+void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                   const bf16* __restrict__ V, const bf16* __restrict__ dO,
+                   const float* __restrict__ LSE, const float* __restrict__ DLT,
+                   bf16* __restrict__ dQ, int Hq, int G, int Sq, int Skv, float scale, float c,
+                   int n_qt) {
+  constexpr int NP = D + 8;
+  constexpr int TP = DQ_BN + 8;
+  constexpr int LTPR = D / 2;
+  constexpr int LGROUPS = DQ_BN / 8;
+  constexpr int LPASSES = (LTPR * LGROUPS + THREADS - 1) / THREADS;
+  static_assert((LTPR * LGROUPS) % THREADS == 0, "K loader must tile the workgroup exactly");
+  constexpr int V_CHUNKS = DQ_BN * D / 8 / THREADS;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[DQ_BN * NP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[DQ_BN * NP];
+  __shared__ __attribute__((aligned(16))) bf16 Kt[D * TP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  int qt = blockIdx.x % n_qt;
+  const int bh = blockIdx.x / n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;
+  const int h = bh % Hq, b = bh / Hq;
+  const int Hkv = Hq / G;
+  const size_t kv_off = ((size_t)(b * Hkv + h / G) * Skv) * D;
+  const int q0 = qt * DQ_BM;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + l32;
+  const int diag = Skv - Sq;
+  const size_t qo = ((size_t)bh * Sq + qrow) * D;
+
+  bf16x8 qf[D / 16], dof[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    qf[s] = as_bf16x8(ld16(Q + qo + 16 * s + 8 * g, qrow < Sq));
+    dof[s] = as_bf16x8(ld16(dO + qo + 16 * s + 8 * g, qrow < Sq));
+  }
+  const float lse2 = qrow < Sq ? LSE[(size_t)bh * Sq + qrow] * MATTN_LOG2E : MATTN_INF;
+  const float dl = qrow < Sq ? DLT[(size_t)bh * Sq + qrow] : 0.f;
+
+  int kv_end = Skv;
+  if (CAUSAL) kv_end = min(Skv, q0 + DQ_BM + diag);
+  const int n_kt = (kv_end + DQ_BN - 1) / DQ_BN;
+
+  DualTile<D, NP, TP> tk[LPASSES];
+  uint4 vreg[V_CHUNKS];
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int ps = 0; ps < LPASSES; ++ps) {
+      const int lt = tid + ps * THREADS;
+      tk[ps].load(K + kv_off + (size_t)j0 * D, 0, Skv - j0, 8 * (lt / LTPR), lt % LTPR);
+    }
+#pragma unroll
+    for (int r = 0; r < V_CHUNKS; ++r) {
+      const int ch = tid + THREADS * r;
+      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      vreg[r] = ld16(V + kv_off + (size_t)(j0 + row) * D + col, j0 + row < Skv);
+    }
+  };
+
+  f32x16 adq[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) adq[db] = zero_f32x16();
+
+  if (n_kt > 0) load_tile(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int j0 = kt * DQ_BN;
+    __syncthreads();
+#pragma unroll
+    for (int ps = 0; ps < LPASSES; ++ps) {
+      const int lt = tid + ps * THREADS;
+      tk[ps].store(Ks, Kt, 8 * (lt / LTPR), lt % LTPR);
+    }
+#pragma unroll
+    for (int r = 0; r < V_CHUNKS; ++r) {
+      const int ch = tid + THREADS * r;
+      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Vs[row * NP + col]) = vreg[r];
+    }
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(j0 + DQ_BN);
+
+    const bool need_mask = (j0 + DQ_BN > Skv) || (CAUSAL && (j0 + DQ_BN - 1 > qw0 + diag));
+    bf16x8 dsb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * NP + 16 * st + 8 * g]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[(kb * 32 + l32) * NP + 16 * st + 8 * g]);
+        s = mfma32(ak, qf[st], s);
+        dp = mfma32(av, dof[st], dp);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
+        if (need_mask) {
+          const int kk = j0 + kb * 32 + crow(i, g);
+          if (kk >= Skv || (CAUSAL && kk > qrow + diag)) p = 0.f;
+        }
+        s[i] = p * (dp[i] - dl);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dsb[kb][t][e] = (bf16)s[8 * t + e];
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(db * 32 + l32) * TP + kb * 32 + 16 * t + 8 * g]);
+          adq[db] = mfma32(a, dsb[kb][t], adq[db]);
+        }
+  }
+
+  if (qrow < Sq) {
+    bf16* prow = dQ + qo;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = db * 32 + r * 8 + g * 4;
+        uint2 w;
+        w.x = pack_bf16x2(adq[db][4 * r] * scale, adq[db][4 * r + 1] * scale);
+        w.y = pack_bf16x2(adq[db][4 * r + 2] * scale, adq[db][4 * r + 3] * scale);
+        *reinterpret_cast<uint2*>(prow + d) = w;
+      }
+  }
+}
+
+template <typename T>
+hipError_t launch_pre_t(const Problem& p, const void* o, const void* dout, float* dlt,
+                        hipStream_t stream) {
+  const long long rows = (long long)p.B * p.Hq * p.Sq;
+  const int tpr = p.D / 8;
+  const long long rpb = THREADS / tpr;
+  const unsigned blocks = (unsigned)((rows + rpb - 1) / rpb);
+  if (p.D == 64)
+    hipLaunchKernelGGL((bwd_pre_kernel<T, 64>), dim3(blocks), dim3(THREADS), 0, stream,
+                       (const T*)o, (const T*)dout, dlt, rows);
+  else
+    hipLaunchKernelGGL((bwd_pre_kernel<T, 128>), dim3(blocks), dim3(THREADS), 0, stream,
+                       (const T*)o, (const T*)dout, dlt, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const void* v,
+                        const float* lse, const float* dlt, const void* dout, void* dq, void* dk,
+                        void* dv, float* part, hipStream_t stream) {
+  const int G = p.Hq / p.Hkv;
+  const float c = p.scale * MATTN_LOG2E;
+  const int n_kt = (p.Skv + BWD_BN - 1) / BWD_BN;
+  const int nsplit = bwd_nsplit(p.B, p.Hkv, p.Sq, p.Skv);
+  const int n_qt32 = (p.Sq + BWD_BMQ - 1) / BWD_BMQ;
+  const int q_chunk = ((n_qt32 + nsplit - 1) / nsplit) * BWD_BMQ;
+  const long long blocks = (long long)p.B * p.Hkv * n_kt * nsplit;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(THREADS), 0,
+                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
+                     lse, dlt, (bf16*)dk, (bf16*)dv, part, p.Hq, G, p.Sq, p.Skv, p.scale, c,
+                     n_kt, nsplit, q_chunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (nsplit > 1) {
+    const long long total4 = (long long)p.B * p.Hkv * p.Skv * D / 4;
+    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((total4 + THREADS - 1) / THREADS)),
+                       dim3(THREADS), 0, stream, (const float*)part, (bf16*)dk, (bf16*)dv, nsplit,
+                       p.B * p.Hkv, p.Skv, n_kt, D, p.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int n_qt = (p.Sq + DQ_BM - 1) / DQ_BM;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * n_qt)),
+                     dim3(THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                     (const bf16*)dout, lse, dlt, (bf16*)dq, p.Hq, G, p.Sq, p.Skv, p.scale, c,
+                     n_qt);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_preprocess(const Problem& p, bool bf16_io, const void* o, const void* dout,
+                                 float* dlt, hipStream_t stream) {
+  return bf16_io ? launch_pre_t<bf16>(p, o, dout, dlt, stream)
+                 : launch_pre_t<float>(p, o, dout, dlt, stream);
+}
+
+hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                           const float* lse, const float* dlt, const void* dout, void* dq,
+                           void* dk, void* dv, float* part, hipStream_t stream) {
+  if (p.D == 64)
+    return p.causal ? launch_bwd_t<64, true>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream)
+                    : launch_bwd_t<64, false>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream);
+  return p.causal ? launch_bwd_t<128, true>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream)
+                  : launch_bwd_t<128, false>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream);
+}
+
+}  // namespace mattn

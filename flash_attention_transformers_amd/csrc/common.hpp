@@ -1,0 +1,114 @@
+// Shared device helpers for the libmattn kernels (gfx950 / CDNA4).
+//
+// Matrix-core building block: v_mfma_f32_32x32x16_bf16, one wave64, fp32
+// accumulate.  Operand layouts (lane l, l32 = l % 32, g = l / 32):
+//   A (32 x 16): lane holds row l32, k = 8g .. 8g+7   (8 bf16, 16 bytes)
+//   B (16 x 32): lane holds col l32, k = 8g .. 8g+7
+//   C (32 x 32): lane holds col l32, rows ((i/4)*8 + 4g + i%4), i = 0..15
+// A C tile can feed the next MFMA as its B operand directly (lane keeps its
+// column): register i = 8t + e of the C tile becomes k-slot 8g + e of k-step
+// t.  The row it carries is 16t + swz(8g + e), where swz swaps bits 2 and 3
+// of a 4-bit index.  The other operand of that MFMA (read from LDS) is
+// therefore stored with its contraction index permuted by swz inside every
+// aligned group of 16; since a contraction is a sum, the order is free.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define MATTN_INF __builtin_huge_valf()
+#define MATTN_LOG2E 1.4426950408889634f
+#define MATTN_LN2 0.6931471805599453f
+
+namespace mattn {
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Swap bits 2 and 3 of the low nibble: position <-> row inside a group of 16.
+__host__ __device__ __forceinline__ constexpr int swz(int x) {
+  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
+}
+
+// Row of the C tile held by register i of lane group g.
+__device__ __forceinline__ constexpr int crow(int i, int g) {
+  return (i >> 2) * 8 + g * 4 + (i & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  bf16x8 z;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
+  return z;
+}
+
+__device__ __forceinline__ f32x16 zero_f32x16() {
+  f32x16 z;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+  return z;
+}
+
+// 16-byte global load of 8 bf16, or zeros when !valid.
+__device__ __forceinline__ uint4 ld16(const bf16* p, bool valid) {
+  if (valid) return *reinterpret_cast<const uint4*>(p);
+  return make_uint4(0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t ld4(const bf16* p, bool valid) {
+  if (valid) return *reinterpret_cast<const uint32_t*>(p);
+  return 0u;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Eight bf16 pairs (d, d+1) of eight rows -> column d and column d+1 as two
+// 8-element vectors (low halves and high halves).
+__device__ __forceinline__ void split_pairs(const uint32_t (&w)[8], uint4& lo, uint4& hi) {
+  uint32_t l[4], h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t a = w[2 * e], b = w[2 * e + 1];
+    l[e] = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (b.lo << 16) | a.lo
+    h[e] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (b.hi << 16) | a.hi
+  }
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16 x = (bf16)a, y = (bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+template <int N>
+__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[base + e];
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+}  // namespace mattn

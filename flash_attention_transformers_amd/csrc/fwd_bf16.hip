@@ -1,0 +1,264 @@
+// Fused attention forward, bf16 I/O, fp32 softmax statistics and accumulation.
+//
+// The method is the fused flash-attention forward of the xtrain evolution
+// page (infrastructure-phase table, row T14): one kernel, an online softmax
+// walking K/V in tiles, the score matrix never materialised.  Grouped KV
+// heads follow row T15 (query head h reads KV head h / G), here by index
+// arithmetic with no repeated K/V.
+//
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+//  * each wave owns 32 query rows and keeps them as the B operand of
+//    S^T = K Q^T in registers for the whole kernel (lane = query column);
+//  * K/V tiles of 64 keys are staged through LDS: K row-major (the A operand
+//    of S^T), V transposed with the swz key order (the A operand of
+//    O^T = V^T P^T), prefetched into registers one tile ahead;
+//  * S^T lands with one query per lane, so the running row max and row sum
+//    are per-lane scalars: 32 in-lane values plus one exchange with lane^32;
+//  * P is rounded to bf16 and fed to the PV MFMA straight from registers;
+//  * O^T accumulates in fp32 registers, one query per lane, so the online
+//    rescale is one multiply by a per-lane factor.
+// Softmax runs in the log2 domain: t = s * scale * log2(e), p = 2^(t - m).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace mattn {
+
+namespace {
+
+constexpr int FWD_BM = 128;
+constexpr int FWD_BN = 64;
+constexpr int FWD_THREADS = 256;
+
+template <int D>
+struct FwdTile {
+  static constexpr int KP = D + 8;        // K row pitch in LDS (bf16)
+  static constexpr int VP = FWD_BN + 8;   // V^T row pitch in LDS (bf16)
+  static constexpr int K_CHUNKS = FWD_BN * D / 8 / FWD_THREADS;  // 16-byte chunks per thread
+  static constexpr int V_TPR = D / 2;                     // threads per key row (2 columns each)
+  static constexpr int V_GROUPS = FWD_THREADS / V_TPR;    // 8-key groups per pass
+  static constexpr int V_PASSES = FWD_BN / (8 * V_GROUPS);
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(FWD_THREADS, 2)
+void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
+                     const bf16* __restrict__ V, bf16* __restrict__ O,
+                     float* __restrict__ LSE, int Hq, int G, int Sq, int Skv,
+                     float c /* scale*log2(e) */, int n_qt) {
+  using T = FwdTile<D>;
+  __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * T::KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vt[D * T::VP];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  int qt = blockIdx.x % n_qt;
+  const int bh = blockIdx.x / n_qt;
+  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  const int h = bh % Hq, b = bh / Hq;
+  const int Hkv = Hq / G;
+  const size_t kv_off = ((size_t)(b * Hkv + h / G) * Skv) * D;
+  const bf16* Qh = Q + (size_t)bh * Sq * D;
+  const bf16* Kh = K + kv_off;
+  const bf16* Vh = V + kv_off;
+
+  const int q0 = qt * FWD_BM;
+  const int qw0 = q0 + wave * 32;          // first query of this wave
+  const int qrow = qw0 + l32;              // this lane's query
+  const int diag = Skv - Sq;               // key j visible to query i iff j <= i + diag
+
+  // Q fragment, B operand of S^T = K Q^T: lane holds q[qrow][16s + 8g .. +7].
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    qf[s] = as_bf16x8(ld16(Qh + (size_t)qrow * D + 16 * s + 8 * g, qrow < Sq));
+
+  int kv_end = Skv;
+  if (CAUSAL) kv_end = min(Skv, q0 + FWD_BM + diag);
+  const int n_kt = (kv_end + FWD_BN - 1) / FWD_BN;
+
+  // Register staging of one K/V tile.
+  uint4 kreg[T::K_CHUNKS];
+  uint32_t vreg[T::V_PASSES][8];
+  const int vc = tid % T::V_TPR, vgrp = tid / T::V_TPR;
+
+  auto load_tile = [&](int j0) {
+#pragma unroll
+    for (int r = 0; r < T::K_CHUNKS; ++r) {
+      const int ch = tid + FWD_THREADS * r;
+      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      kreg[r] = ld16(Kh + (size_t)(j0 + row) * D + col, j0 + row < Skv);
+    }
+#pragma unroll
+    for (int p = 0; p < T::V_PASSES; ++p) {
+      const int pos0 = 8 * (p * T::V_GROUPS + vgrp);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int pos = pos0 + e;
+        const int key = j0 + (pos & ~15) + swz(pos & 15);
+        vreg[p][e] = ld4(Vh + (size_t)key * D + 2 * vc, key < Skv);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int r = 0; r < T::K_CHUNKS; ++r) {
+      const int ch = tid + FWD_THREADS * r;
+      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Ks[row * T::KP + col]) = kreg[r];
+    }
+#pragma unroll
+    for (int p = 0; p < T::V_PASSES; ++p) {
+      const int pos0 = 8 * (p * T::V_GROUPS + vgrp);
+      uint4 lo, hi;
+      split_pairs(vreg[p], lo, hi);
+      *reinterpret_cast<uint4*>(&Vt[(2 * vc) * T::VP + pos0]) = lo;
+      *reinterpret_cast<uint4*>(&Vt[(2 * vc + 1) * T::VP + pos0]) = hi;
+    }
+  };
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = zero_f32x16();
+  float m = -MATTN_INF;  // running max of t over this query's keys (shared by lane, lane^32)
+  float l = 0.f;         // this lane's partial row sum (relative to m)
+
+  if (n_kt > 0) load_tile(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int j0 = kt * FWD_BN;
+    __syncthreads();
+    store_tile();
+    __syncthreads();
+    if (kt + 1 < n_kt) load_tile(j0 + FWD_BN);
+
+    // S^T for two 32-key blocks: lane = query column, regs = keys.
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 s = zero_f32x16();
+#pragma unroll
+      for (int st = 0; st < D / 16; ++st) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * T::KP + 16 * st + 8 * g]);
+        s = mfma32(a, qf[st], s);
+      }
+      sc[kb] = s;
+    }
+
+    const bool need_mask = (j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag));
+    float mt;
+    if (!need_mask && c > 0.f) {
+      float mx = -MATTN_INF;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+      mt = mx * c;
+    } else {
+      // Convert to t = s*c in place; masked keys become -inf.
+      float mx = -MATTN_INF;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = j0 + kb * 32 + crow(i, g);
+          const bool ok = key < Skv && (!CAUSAL || key <= qrow + diag);
+          const float t = ok ? sc[kb][i] * c : -MATTN_INF;
+          sc[kb][i] = t;
+          mx = fmaxf(mx, t);
+        }
+      mt = mx;
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = fmaxf(m, mt);
+    const float m_use = (m_new == -MATTN_INF) ? 0.f : m_new;
+    const float alpha = fast_exp2(m - m_use);
+    m = m_new;
+
+    float rs = 0.f;
+    if (!need_mask && c > 0.f) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(sc[kb][i], c, -m_use));
+          sc[kb][i] = p;
+          rs += p;
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(sc[kb][i] - m_use);
+          sc[kb][i] = p;
+          rs += p;
+        }
+    }
+    l = l * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[kb][t][e] = (bf16)sc[kb][8 * t + e];
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              &Vt[(db * 32 + l32) * T::VP + kb * 32 + 16 * t + 8 * g]);
+          acc[db] = mfma32(a, pb[kb][t], acc[db]);
+        }
+  }
+
+  l += __shfl_xor(l, 32);
+  if (qrow < Sq) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    bf16* orow = O + ((size_t)bh * Sq + qrow) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = db * 32 + r * 8 + g * 4;
+        uint2 w;
+        w.x = pack_bf16x2(acc[db][4 * r + 0] * inv, acc[db][4 * r + 1] * inv);
+        w.y = pack_bf16x2(acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + d) = w;
+      }
+    if (g == 0)
+      LSE[(size_t)bh * Sq + qrow] = l > 0.f ? (m + log2f(l)) * MATTN_LN2 : -MATTN_INF;
+  }
+}
+
+}  // namespace
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v,
+                             void* o, float* lse, hipStream_t stream) {
+  const int n_qt = (p.Sq + FWD_BM - 1) / FWD_BM;
+  const long long blocks = (long long)p.B * p.Hq * n_qt;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(FWD_THREADS), 0,
+                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, p.Hq,
+                     p.Hq / p.Hkv, p.Sq, p.Skv, p.scale * MATTN_LOG2E, n_qt);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                           void* o, float* lse, hipStream_t stream) {
+  if (p.D == 64) return p.causal ? launch_fwd<64, true>(p, q, k, v, o, lse, stream)
+                                 : launch_fwd<64, false>(p, q, k, v, o, lse, stream);
+  return p.causal ? launch_fwd<128, true>(p, q, k, v, o, lse, stream)
+                  : launch_fwd<128, false>(p, q, k, v, o, lse, stream);
+}
+
+}  // namespace mattn

@@ -1,0 +1,109 @@
+/*
+ * libmattn — fused scaled-dot-product attention with online softmax for
+ * AMD Instinct MI355X (gfx950), forward and flash-style backward.
+ *
+ * The operation is the one the xtrain evolution page describes in its
+ * infrastructure-phase table, row T14: a single fused forward kernel with an
+ * online softmax that walks K/V in tiles and never materialises the
+ * Sq x Skv score matrix, and a backward that recomputes the scores and uses
+ * the per-row scalar D = sum(dO * O) to simplify the softmax Jacobian before
+ * forming dQ, dK and dV.  Grouped KV heads follow row T15 of that table:
+ * query head h reads KV head floor(h / G), G = Hq / Hkv, and each KV head's
+ * gradient is the deterministic sum over its G query heads (no atomics).
+ *
+ * Math, for every batch b, query head h, kv = h / G, query row i, key j:
+ *   S_ij = scale * sum_d q[b,h,i,d] * k[b,kv,j,d]     (-inf where masked)
+ *   P_ij = softmax_j(S_ij);   o[b,h,i,:] = sum_j P_ij v[b,kv,j,:]
+ *   lse[b,h,i] = ln sum_j exp(S_ij)                  (natural log)
+ * Causal masking is aligned bottom-right: key j is visible to query i iff
+ * j <= i + (Skv - Sq).
+ *
+ * Layout: every tensor is dense, row-major, contiguous BHSD:
+ *   q, o, dout, dq : [B, Hq,  Sq,  D]
+ *   k, v, dk, dv   : [B, Hkv, Skv, D]
+ *   lse            : [B, Hq,  Sq]     float32
+ * Element type: MATTN_BF16 (bfloat16 I/O, float32 softmax statistics and
+ * accumulation, outputs rounded to nearest even) or MATTN_F32 (float32
+ * throughout; no operand is rounded below float32).
+ *
+ * Ownership: every pointer is a device pointer owned by the caller.  The
+ * library allocates nothing, keeps no global state, never synchronises the
+ * device and is safe to call from several host threads.  Work is enqueued on
+ * `stream` (0 = the null stream) and runs asynchronously; buffers must stay
+ * alive until the stream reaches that point.  Outputs must not alias inputs
+ * and are fully overwritten (never accumulated into).
+ *
+ * Errors: all argument checks are synchronous and happen before anything is
+ * enqueued; on any error nothing is launched and no output is written.
+ *   MATTN_ERR_INVALID_ARG  a null or misaligned pointer that the call needs (all
+ *                          of them when B*Hq*Sq > 0; with no query rows the
+ *                          backward needs only dk and dv), a size < 0,
+ *                          Hkv == 0 or Hq % Hkv != 0, Skv == 0 with Sq > 0,
+ *                          causal not 0/1, a non-finite scale (pointers must be
+ *                          16-byte aligned), an unknown dtype, or (backward) a
+ *                          workspace smaller than mattn_bwd_workspace_size().
+ *   MATTN_ERR_UNSUPPORTED  D not 64 or 128, a tensor with 2^31 or more
+ *                          elements, or causal with Sq > Skv (which would
+ *                          leave query rows with no visible key).
+ *   MATTN_ERR_LAUNCH       the HIP runtime reported an error after a launch.
+ * B*Hq*Sq == 0 with otherwise valid sizes returns MATTN_OK: the forward does
+ * nothing and the backward writes zeros to dk and dv.
+ */
+#ifndef MATTN_H
+#define MATTN_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MATTN_OK = 0,
+  MATTN_ERR_INVALID_ARG = 1,
+  MATTN_ERR_UNSUPPORTED = 2,
+  MATTN_ERR_LAUNCH = 3
+} mattn_status;
+
+typedef enum { MATTN_BF16 = 0, MATTN_F32 = 1 } mattn_dtype;
+
+/* Forward: o = softmax(scale * q k^T, masked) v and its log-sum-exp.
+ * q [B,Hq,Sq,D], k/v [B,Hkv,Skv,D] in `dtype`; writes o [B,Hq,Sq,D] in
+ * `dtype` and lse [B,Hq,Sq] float32.  One kernel launch. */
+mattn_status mattn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                       float scale, mattn_dtype dtype, hipStream_t stream);
+
+/* Bytes of device workspace mattn_bwd needs for these sizes: the per-row
+ * D = sum(dO * O) statistic (B*Hq*Sq float32) plus, for shapes with few KV
+ * tiles, float32 partial dK/dV over fixed chunks of the query range.  Rounded
+ * up to 256 bytes; depends only on the arguments.  Returns 0 for invalid or
+ * empty sizes. */
+size_t mattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D);
+
+/* Backward of mattn_fwd for the loss gradient dout = dL/do.
+ * Inputs: q, k, v, the forward's o and lse, dout.  Writes dq [B,Hq,Sq,D] and
+ * dk, dv [B,Hkv,Skv,D] in `dtype` (overwritten).  `workspace` is caller-owned
+ * device memory of at least mattn_bwd_workspace_size() bytes; its contents on
+ * entry do not matter.  Enqueues, on `stream` and with no host
+ * synchronisation: the D = sum(dO * O) preprocess, the dK/dV kernel (plus a
+ * fixed-order reduction of partials when the query range is split) and the dQ
+ * kernel.  Results are bitwise reproducible run to run. */
+mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                       int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                       float scale, mattn_dtype dtype, void* workspace,
+                       size_t workspace_bytes, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* mattn_strerror(mattn_status s);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int mattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MATTN_H */

@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU work is launched).
+
+The library must load, export every function include/mattn.h declares, and
+reject invalid arguments synchronously, before touching the device.  Pointer
+arguments here are fake aligned addresses: every call either fails
+validation or describes an empty problem, so nothing is ever dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import flash_attention_transformers_amd as fa
+from flash_attention_transformers_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mattn.h")
+P = 0x10000  # fake, 16-byte aligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(mattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted(
+        ["mattn_fwd", "mattn_bwd", "mattn_bwd_workspace_size", "mattn_strerror", "mattn_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strerror():
+    assert fa.mattn_version() >= 100
+    assert fa.mattn_strerror(0) == "success"
+    for s in (1, 2, 3):
+        assert fa.mattn_strerror(s) and fa.mattn_strerror(s) != "success"
+    assert fa.mattn_strerror(99) == "unknown status"
+
+
+def fwd_status(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=2, Hkv=2, Sq=128, Skv=128, D=64, causal=0,
+               scale=0.125, dtype=0):
+    lib = fa.load_library()
+    return lib.mattn_fwd(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, dtype, None)
+
+
+def bwd_status(ws=P, ws_bytes=1 << 40, B=1, Hq=2, Hkv=2, Sq=128, Skv=128, D=64, causal=0,
+               scale=0.125, dtype=0, dq=P, q=P):
+    lib = fa.load_library()
+    return lib.mattn_bwd(q, P, P, P, P, P, dq, P, P, B, Hq, Hkv, Sq, Skv, D, causal, scale, dtype,
+                         ws, ws_bytes, None)
+
+
+INVALID = [
+    dict(B=-1), dict(Sq=-3), dict(Hkv=0), dict(Hq=6, Hkv=4), dict(causal=2),
+    dict(scale=float("nan")), dict(scale=float("inf")), dict(dtype=7), dict(Skv=0),
+    dict(q=0), dict(lse=0), dict(o=P + 8),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID)
+def test_fwd_rejects_invalid(kw):
+    assert fwd_status(**kw) == fa.MATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(D=96), dict(D=256), dict(causal=1, Sq=129, Skv=128),
+                                dict(B=1 << 12, Hq=1 << 8, Hkv=1 << 8, Sq=1 << 8, D=128)])
+def test_fwd_rejects_unsupported(kw):
+    assert fwd_status(**kw) == fa.MATTN_ERR_UNSUPPORTED
+
+
+def test_empty_problem_is_a_noop():
+    assert fwd_status(B=0) == fa.MATTN_OK
+    assert fwd_status(Sq=0, q=0, o=0, lse=0, k=0, v=0, Skv=0) == fa.MATTN_OK
+
+
+@pytest.mark.parametrize("kw", [dict(ws=0), dict(ws_bytes=16), dict(ws=P + 4), dict(dq=0),
+                                dict(Hq=3, Hkv=2), dict(causal=-1)])
+def test_bwd_rejects_invalid(kw):
+    assert bwd_status(**kw) == fa.MATTN_ERR_INVALID_ARG
+
+
+def test_bwd_rejects_unsupported():
+    assert bwd_status(D=32) == fa.MATTN_ERR_UNSUPPORTED
+    assert bwd_status(causal=1, Sq=300, Skv=200) == fa.MATTN_ERR_UNSUPPORTED
+
+
+def test_workspace_size():
+    ws = fa.mattn_bwd_workspace_size
+    assert ws(0, 2, 2, 128, 128, 64) == 0
+    assert ws(1, 3, 2, 128, 128, 64) == 0
+    assert ws(1, 2, 2, 128, 128, 96) == 0
+    # the per-row statistic only, rounded to 256 bytes
+    assert ws(8, 12, 12, 1024, 1024, 64) == 8 * 12 * 1024 * 4
+    assert ws(1, 1, 1, 3, 5, 64) == 256
+    # short-KV cross attention adds fp32 partial dK/dV for split query chunks
+    w = W.WORKLOADS["dit_cross_512"]
+    n = ws(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D)
+    dlt = w.B * w.Hq * w.Sq * 4
+    part = n - ((dlt + 255) // 256 * 256)
+    per_split = 2 * w.B * w.Hkv * 512 * w.D * 4
+    assert part > 0 and part % per_split == 0
+    assert ws(w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D) == n  # deterministic
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q, q)

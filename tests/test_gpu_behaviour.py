@@ -1,0 +1,201 @@
+"""GPU behaviour beyond parity: determinism, NaN-poisoned tails and guard
+words, GQA versus repeated-KV MHA, invariants, rejection and empty problems.
+All calls go through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+
+import flash_attention_transformers_amd as fa
+from flash_attention_transformers_amd import workloads as W
+
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    fa.load_library()
+    return torch.device("cuda:0")
+
+
+def fwd_bwd(t, causal, scale=None):
+    o, lse = fa.fwd(t["q"], t["k"], t["v"], causal=causal, scale=scale)
+    dq, dk, dv = fa.bwd(t["q"], t["k"], t["v"], o, lse, t["do"], causal=causal, scale=scale)
+    return dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+
+
+@pytest.mark.parametrize("shape", [(2, 8, 2, 700, 700, 128, True), (1, 4, 4, 2000, 200, 128, False),
+                                   (2, 4, 4, 300, 300, 64, True)])
+def test_bitwise_determinism(shape, dev):
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D, causal = shape
+    H.say(f"[determinism] {shape}")
+    w = W.Workload("det", B, Hq, Hkv, Sq, Skv, D, causal, "bf16", 9, True)
+    t = W.to_torch(W.make_inputs(w), dev)
+    a = fwd_bwd(t, causal)
+    b = fwd_bwd(t, causal)
+    torch.cuda.synchronize()
+    for n in a:
+        assert torch.equal(a[n].view(torch.int16) if a[n].dtype == torch.bfloat16 else a[n],
+                           b[n].view(torch.int16) if b[n].dtype == torch.bfloat16 else b[n]), n
+
+
+def _poisoned(t, pad):
+    """Copy t into the middle of a NaN-filled buffer; return (view, buffer)."""
+    import torch
+
+    n = t.numel()
+    buf = torch.full((n + 2 * pad,), float("nan"), dtype=t.dtype, device=t.device)
+    buf[pad:pad + n] = t.reshape(-1)
+    return buf[pad:pad + n].view(t.shape), buf
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 64)])
+def test_nan_poisoned_tails_and_guards(dtype, D, dev):
+    import torch
+
+    H.say(f"[nan guards] {dtype} D={D}")
+    w = W.Workload("guard", 1, 2, 1, 131, 257, D, False, dtype, 11, True)
+    t = W.to_torch(W.make_inputs(w), dev)
+    clean = fwd_bwd(t, False)
+    pad = 4096  # elements of NaN before and after every input
+    tp, bufs = {}, []
+    for n in ("q", "k", "v", "do"):
+        tp[n], buf = _poisoned(t[n], pad)
+        bufs.append(buf)
+    # outputs: NaN-prefilled with NaN guard regions on both sides
+    outs = {}
+    for n, like in (("o", t["q"]), ("dq", t["q"]), ("dk", t["k"]), ("dv", t["v"])):
+        outs[n] = _poisoned(torch.full_like(like, float("nan")), pad)
+    lse_v, lse_buf = _poisoned(torch.full((1, 2, 131), float("nan"), device=dev), pad)
+    fa.mattn_fwd(tp["q"], tp["k"], tp["v"], outs["o"][0], lse_v, False, None)
+    ws = fa.bwd_workspace(tp["q"], tp["k"])
+    ws.fill_(255)  # contents on entry must not matter
+    fa.mattn_bwd(tp["q"], tp["k"], tp["v"], outs["o"][0], lse_v, tp["do"], outs["dq"][0],
+                 outs["dk"][0], outs["dv"][0], ws, False, None)
+    torch.cuda.synchronize()
+    for n in ("o", "dq", "dk", "dv"):
+        view, buf = outs[n]
+        assert torch.isfinite(view).all(), n
+        a, b = view, clean[n]
+        if a.dtype == torch.bfloat16:
+            a, b = a.view(torch.int16), b.view(torch.int16)
+        assert torch.equal(a, b), n
+        assert torch.isnan(buf[:pad]).all() and torch.isnan(buf[-pad:]).all(), f"guard {n}"
+    assert torch.equal(lse_v, clean["lse"])
+    assert torch.isnan(lse_buf[:pad]).all() and torch.isnan(lse_buf[-pad:]).all()
+
+
+def test_gqa_matches_repeated_kv(dev):
+    import torch
+
+    H.say("[gqa vs repeated kv]")
+    G = 4
+    w = W.Workload("gqa", 2, 8, 2, 260, 260, 128, True, "bf16", 13, True)
+    t = W.to_torch(W.make_inputs(w), dev)
+    a = fwd_bwd(t, True)
+    tr = dict(t)
+    tr["k"] = t["k"].repeat_interleave(G, dim=1).contiguous()
+    tr["v"] = t["v"].repeat_interleave(G, dim=1).contiguous()
+    b = fwd_bwd(tr, True)
+    torch.cuda.synchronize()
+    # the forward of a query head does identical arithmetic either way
+    assert torch.equal(a["o"].view(torch.int16), b["o"].view(torch.int16))
+    assert torch.equal(a["lse"], b["lse"])
+    assert torch.equal(a["dq"].view(torch.int16), b["dq"].view(torch.int16))
+    for n in ("dk", "dv"):
+        summed = b[n].float().view(2, 2, G, 260, 128).sum(2)
+        assert H.rel_l2(a[n].float().cpu().numpy(), summed.cpu().numpy().astype(np.float64)) < 1e-2, n
+
+
+def test_gradient_sum_invariants(dev):
+    # sum_j dK_j = 0 and sum_j dV_j = sum over the group's query rows of dO
+    H.say("[invariants]")
+    w = W.Workload("inv", 1, 4, 2, 256, 256, 64, True, "bf16", 17, True)
+    inp = W.make_inputs(w)
+    t = W.to_torch(inp, dev)
+    g = fwd_bwd(t, True)
+    dk = g["dk"].float().cpu().numpy().astype(np.float64)
+    dv = g["dv"].float().cpu().numpy().astype(np.float64)
+    s_dk = dk.sum(2)
+    assert np.abs(s_dk).max() <= 2e-2 * np.abs(dk).sum(2).max()
+    want = inp.vals["do"].astype(np.float64).reshape(1, 2, 2, 256, 64).sum((2, 3))
+    assert np.abs(dv.sum(2) - want).max() <= 2e-2 * np.abs(want).max()
+
+
+def test_rejection_leaves_outputs_untouched(dev):
+    import torch
+
+    H.say("[rejection]")
+    q = torch.randn(1, 3, 64, 64, device=dev, dtype=torch.bfloat16)
+    k = torch.randn(1, 2, 64, 64, device=dev, dtype=torch.bfloat16)  # 3 % 2 != 0
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 3, 64), float("nan"), device=dev)
+    with pytest.raises(fa.MattnError) as e:
+        fa.mattn_fwd(q, k, k, o, lse)
+    assert e.value.status == fa.MATTN_ERR_INVALID_ARG
+    q96 = torch.randn(1, 2, 64, 96, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(fa.MattnError) as e:
+        fa.fwd(q96, q96, q96)
+    assert e.value.status == fa.MATTN_ERR_UNSUPPORTED
+    qc = torch.randn(1, 2, 65, 64, device=dev, dtype=torch.bfloat16)
+    kc = torch.randn(1, 2, 64, 64, device=dev, dtype=torch.bfloat16)
+    oc = torch.full_like(qc, float("nan"))
+    lc = torch.full((1, 2, 65), float("nan"), device=dev)
+    with pytest.raises(fa.MattnError) as e:
+        fa.mattn_fwd(qc, kc, kc, oc, lc, causal=True)
+    assert e.value.status == fa.MATTN_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert torch.isnan(o.float()).all() and torch.isnan(lse).all()
+    assert torch.isnan(oc.float()).all() and torch.isnan(lc).all()
+
+
+def test_empty_problems(dev):
+    import torch
+
+    H.say("[empty]")
+    q = torch.empty(0, 2, 16, 64, device=dev, dtype=torch.bfloat16)
+    o, lse = fa.fwd(q, q, q)
+    assert o.numel() == 0
+    # no query rows: every key's gradient is zero
+    q0 = torch.empty(1, 2, 0, 64, device=dev, dtype=torch.bfloat16)
+    k = torch.randn(1, 2, 40, 64, device=dev, dtype=torch.bfloat16)
+    o0 = torch.empty_like(q0)
+    l0 = torch.empty(1, 2, 0, device=dev)
+    dq = torch.empty_like(q0)
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(k, float("nan"))
+    ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    fa.mattn_bwd(q0, k, k, o0, l0, q0, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    assert (dk.float() == 0).all() and (dv.float() == 0).all()
+
+
+def test_negative_and_zero_scale(dev):
+    H.say("[scale sign]")
+    for scale in (-0.3, 0.0):
+        for dtype in ("bf16", "f32"):
+            w = W.Workload("scale", 1, 2, 2, 150, 90, 64, False, dtype, 19, True)
+            inp = W.make_inputs(w)
+            t = W.to_torch(inp, dev)
+            g = fwd_bwd(t, False, scale=scale)
+            import oracle
+
+            v = inp.vals
+            ro, _ = oracle.attention_forward(v["q"], v["k"], v["v"], False, scale)
+            rdq, rdk, rdv, _ = oracle.attention_backward(v["q"], v["k"], v["v"], v["do"], False, scale)
+            tol = H.TOL[dtype]
+            assert H.max_abs(H.to_np(g["o"]), ro) <= tol["o_max_abs"]
+            assert H.rel_l2(H.to_np(g["dv"]), rdv) <= tol["grad_rel_l2"]
+            if scale != 0.0:
+                assert H.rel_l2(H.to_np(g["dq"]), rdq) <= tol["grad_rel_l2"]
+                assert H.rel_l2(H.to_np(g["dk"]), rdk) <= tol["grad_rel_l2"]
+            else:
+                assert np.abs(H.to_np(g["dq"])).max() == 0 and np.abs(H.to_np(g["dk"])).max() == 0
