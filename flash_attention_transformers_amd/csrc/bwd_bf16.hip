@@ -68,19 +68,20 @@ void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
 }
 
 // ----------------------------------------------------------------------------
-// Load 8 rows x 2 columns of a [rows x D] bf16 tile with 4-byte loads and
-// write it to LDS twice: row-major (pitch NP) and transposed with the swz row
-// order (pitch TP).  `pos0` is the first (multiple-of-8) transposed position;
-// the rows it covers are (pos & ~15) + swz(pos & 15).
+// Load 8 rows x 2 columns of a [rows x D] bf16 tile with 4-byte buffer loads
+// (rows past the descriptor's range read as zero) and write it to LDS twice:
+// row-major (pitch NP) and transposed with the swz row order (pitch TP).
+// `pos0` is the first (multiple-of-8) transposed position; the rows it covers
+// are (pos & ~15) + swz(pos & 15).
 template <int D, int NP, int TP>
 struct DualTile {
   uint32_t w[8];
-  __device__ __forceinline__ void load(const bf16* base, int row0, int nrows_valid, int pos0, int c2) {
+  __device__ __forceinline__ void load(const Buf& src, int row0, int pos0, int c2) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int pos = pos0 + e;
       const int r = (pos & ~15) + swz(pos & 15);
-      w[e] = ld4(base + (size_t)(row0 + r) * D + 2 * c2, r < nrows_valid);
+      w[e] = src.ld4((uint32_t)((row0 + r) * D + 2 * c2) * 2);
     }
   }
   __device__ __forceinline__ void store(bf16* nat, bf16* tr, int pos0, int c2) const {
@@ -107,13 +108,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, float* __restrict__ part,
                      int Hq, int G, int Sq, int Skv, float scale, float c, int n_kt,
                      int nsplit, int q_chunk) {
-  constexpr int BMQ = BWD_BMQ;
+  constexpr int BMQ = BWD_BMQ;            // query rows per step (two 32-row sub-blocks)
+  constexpr int NSUB = BMQ / 32;
   constexpr int NP = D + 8;
   constexpr int TP = BMQ + 8;
-  constexpr int LTPR = D / 2;             // loader threads per row pair-column set
-  constexpr int LGROUPS = BMQ / 8;        // 8-row groups per tile
-  constexpr int LTHREADS = LTPR * LGROUPS;
-  static_assert(LTHREADS <= THREADS, "tile loader needs more threads than the workgroup has");
+  constexpr int LTPR = D / 2;             // loader threads per 8-row group (2 columns each)
+  constexpr int LGROUPS = BMQ / 8;
+  constexpr int LPASSES = LTPR * LGROUPS / THREADS;
+  static_assert((LTPR * LGROUPS) % THREADS == 0, "tile loader must tile the workgroup");
   __shared__ __attribute__((aligned(16))) bf16 Qs[BMQ * NP];
   __shared__ __attribute__((aligned(16))) bf16 dOs[BMQ * NP];
   __shared__ __attribute__((aligned(16))) bf16 Qt[D * TP];
@@ -136,11 +138,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int diag = Skv - Sq;
 
   const size_t kv_off = (size_t)bkv * Skv * D;
+  const Buf kbuf(K + kv_off, (uint32_t)Skv * D * 2);
+  const Buf vbuf(V + kv_off, (uint32_t)Skv * D * 2);
   bf16x8 kf[D / 16], vf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    kf[s] = as_bf16x8(ld16(K + kv_off + (size_t)key * D + 16 * s + 8 * g, key < Skv));
-    vf[s] = as_bf16x8(ld16(V + kv_off + (size_t)key * D + 16 * s + 8 * g, key < Skv));
+    kf[s] = as_bf16x8(kbuf.ld16((uint32_t)(key * D + 16 * s + 8 * g) * 2));
+    vf[s] = as_bf16x8(vbuf.ld16((uint32_t)(key * D + 16 * s + 8 * g) * 2));
   }
   f32x16 adk[D / 32], adv[D / 32];
 #pragma unroll
@@ -160,26 +164,28 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int nq = qe > q_lo ? (qe - q_lo + BMQ - 1) / BMQ : 0;
   const int n_it = G * nq;
 
-  const bool loader = tid < LTHREADS;
-  const int c2 = tid % LTPR, pos0 = 8 * (tid / LTPR);
-  DualTile<D, NP, TP> tq, tdo;
+  DualTile<D, NP, TP> tq[LPASSES], tdo[LPASSES];
   float pre_lse = 0.f, pre_dlt = 0.f;
 
   auto load_it = [&](int it) {
-    const int r = it / nq, qi = it % nq;
+    const int r = it / nq, qi = it - r * nq;
     const int h = kvh * G + r;
     const int qt0 = q_lo + qi * BMQ;
-    const size_t q_off = ((size_t)(b * Hq + h) * Sq + qt0) * D;
-    const int nvalid = Sq - qt0;
-    if (loader) {
-      tq.load(Q + q_off, 0, nvalid, pos0, c2);
-      tdo.load(dO + q_off, 0, nvalid, pos0, c2);
+    const size_t hoff = (size_t)(b * Hq + h) * Sq;
+    // Rows at or past Sq fall outside the descriptors and load as zeros.
+    const Buf qbuf(Q + hoff * D, (uint32_t)Sq * D * 2);
+    const Buf dobuf(dO + hoff * D, (uint32_t)Sq * D * 2);
+#pragma unroll
+    for (int ps = 0; ps < LPASSES; ++ps) {
+      const int lt = tid + ps * THREADS;
+      tq[ps].load(qbuf, qt0, 8 * (lt / LTPR), lt % LTPR);
+      tdo[ps].load(dobuf, qt0, 8 * (lt / LTPR), lt % LTPR);
     }
     if (tid < BMQ) {
-      const int qq = qt0 + tid;
-      const size_t ro = (size_t)(b * Hq + h) * Sq + qq;
-      pre_lse = qq < Sq ? LSE[ro] * MATTN_LOG2E : MATTN_INF;
-      pre_dlt = qq < Sq ? DLT[ro] : 0.f;
+      const Buf lbuf(LSE + hoff, (uint32_t)Sq * 4);
+      const Buf dbuf(DLT + hoff, (uint32_t)Sq * 4);
+      pre_lse = lbuf.ldf((uint32_t)(qt0 + tid) * 4);
+      pre_dlt = dbuf.ldf((uint32_t)(qt0 + tid) * 4);
     }
   };
 
@@ -187,58 +193,76 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   for (int it = 0; it < n_it; ++it) {
     const int qt0 = q_lo + (it % nq) * BMQ;
     __syncthreads();
-    if (loader) {
-      tq.store(Qs, Qt, pos0, c2);
-      tdo.store(dOs, dOt, pos0, c2);
+#pragma unroll
+    for (int ps = 0; ps < LPASSES; ++ps) {
+      const int lt = tid + ps * THREADS;
+      tq[ps].store(Qs, Qt, 8 * (lt / LTPR), lt % LTPR);
+      tdo[ps].store(dOs, dOt, 8 * (lt / LTPR), lt % LTPR);
     }
     if (tid < BMQ) {
-      lse_s[tid] = pre_lse;
-      dlt_s[tid] = pre_dlt;
+      // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
+      const bool real = qt0 + tid < Sq;
+      lse_s[tid] = real ? pre_lse * MATTN_LOG2E : MATTN_INF;
+      dlt_s[tid] = real ? pre_dlt : 0.f;
     }
     __syncthreads();
     if (it + 1 < n_it) load_it(it + 1);
 
-    // S = Q K^T and dP = dO V^T: lane = key column, regs = query rows.
-    f32x16 s = zero_f32x16(), dp = zero_f32x16();
+    // S = Q K^T and dP = dO V^T per 32-row sub-block: lane = key column,
+    // regs = query rows.
+    f32x16 s[NSUB], dp[NSUB];
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[l32 * NP + 16 * st + 8 * g]);
-      const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dOs[l32 * NP + 16 * st + 8 * g]);
-      s = mfma32(aq, kf[st], s);
-      dp = mfma32(ad, vf[st], dp);
+    for (int qb = 0; qb < NSUB; ++qb) {
+      s[qb] = zero_f32x16();
+      dp[qb] = zero_f32x16();
     }
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+      for (int qb = 0; qb < NSUB; ++qb) {
+        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[(qb * 32 + l32) * NP + 16 * st + 8 * g]);
+        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dOs[(qb * 32 + l32) * NP + 16 * st + 8 * g]);
+        s[qb] = mfma32(aq, kf[st], s[qb]);
+        dp[qb] = mfma32(ad, vf[st], dp[qb]);
+      }
     const bool need_mask = CAUSAL && (kw0 + 31 > qt0 + diag);
+    bf16x8 pb[NSUB][2], dsb[NSUB][2];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const f32x4 L = *reinterpret_cast<const f32x4*>(&lse_s[8 * blk + 4 * g]);
-      const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[8 * blk + 4 * g]);
+    for (int qb = 0; qb < NSUB; ++qb) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * blk + j;
-        float p = fast_exp2(__builtin_fmaf(s[i], c, -L[j]));
-        if (need_mask && key > qt0 + crow(i, g) + diag) p = 0.f;
-        s[i] = p;
-        dp[i] = p * (dp[i] - Dl[j]);
+      for (int blk = 0; blk < 4; ++blk) {
+        const f32x4 L = *reinterpret_cast<const f32x4*>(&lse_s[qb * 32 + 8 * blk + 4 * g]);
+        const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[qb * 32 + 8 * blk + 4 * g]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * blk + j;
+          float p = fast_exp2(__builtin_fmaf(s[qb][i], c, -L[j]));
+          if (need_mask && key > qt0 + qb * 32 + crow(i, g) + diag) p = 0.f;
+          s[qb][i] = p;
+          dp[qb][i] = p * (dp[qb][i] - Dl[j]);
+        }
       }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[qb][t][e] = (bf16)s[qb][8 * t + e];
+          dsb[qb][t][e] = (bf16)dp[qb][8 * t + e];
+        }
     }
-    bf16x8 pb[2], dsb[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[t][e] = (bf16)s[8 * t + e];
-        dsb[t][e] = (bf16)dp[8 * t + e];
-      }
     // dV^T += dO^T P, dK^T += Q^T dS.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int qb = 0; qb < NSUB; ++qb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const bf16x8 ado = *reinterpret_cast<const bf16x8*>(&dOt[(db * 32 + l32) * TP + 16 * t + 8 * g]);
-        const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(&Qt[(db * 32 + l32) * TP + 16 * t + 8 * g]);
-        adv[db] = mfma32(ado, pb[t], adv[db]);
-        adk[db] = mfma32(aqt, dsb[t], adk[db]);
-      }
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const int col = qb * 32 + 16 * t + 8 * g;
+          const bf16x8 ado = *reinterpret_cast<const bf16x8*>(&dOt[(db * 32 + l32) * TP + col]);
+          const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(&Qt[(db * 32 + l32) * TP + col]);
+          adv[db] = mfma32(ado, pb[qb][t], adv[db]);
+          adk[db] = mfma32(aqt, dsb[qb][t], adk[db]);
+        }
   }
 
   if (key >= Skv) return;
@@ -330,9 +354,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  int qt = blockIdx.x % n_qt;
-  const int bh = blockIdx.x / n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;
+  int bh, qt;
+  tile_of_block(blockIdx.x, gridDim.x / n_qt, n_qt, CAUSAL, bh, qt);
   const int h = bh % Hq, b = bh / Hq;
   const int Hkv = Hq / G;
   const size_t kv_off = ((size_t)(b * Hkv + h / G) * Skv) * D;
@@ -342,12 +365,17 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int diag = Skv - Sq;
   const size_t qo = ((size_t)bh * Sq + qrow) * D;
 
+  const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
+  const Buf dobuf(dO + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
+  const Buf kbuf(K + kv_off, (uint32_t)Skv * D * 2);
+  const Buf vbuf(V + kv_off, (uint32_t)Skv * D * 2);
   bf16x8 qf[D / 16], dof[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
-    qf[s] = as_bf16x8(ld16(Q + qo + 16 * s + 8 * g, qrow < Sq));
-    dof[s] = as_bf16x8(ld16(dO + qo + 16 * s + 8 * g, qrow < Sq));
+    qf[s] = as_bf16x8(qbuf.ld16((uint32_t)(qrow * D + 16 * s + 8 * g) * 2));
+    dof[s] = as_bf16x8(dobuf.ld16((uint32_t)(qrow * D + 16 * s + 8 * g) * 2));
   }
+  // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
   const float lse2 = qrow < Sq ? LSE[(size_t)bh * Sq + qrow] * MATTN_LOG2E : MATTN_INF;
   const float dl = qrow < Sq ? DLT[(size_t)bh * Sq + qrow] : 0.f;
 
@@ -361,13 +389,13 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
     for (int ps = 0; ps < LPASSES; ++ps) {
       const int lt = tid + ps * THREADS;
-      tk[ps].load(K + kv_off + (size_t)j0 * D, 0, Skv - j0, 8 * (lt / LTPR), lt % LTPR);
+      tk[ps].load(kbuf, j0, 8 * (lt / LTPR), lt % LTPR);
     }
 #pragma unroll
     for (int r = 0; r < V_CHUNKS; ++r) {
       const int ch = tid + THREADS * r;
       const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      vreg[r] = ld16(V + kv_off + (size_t)(j0 + row) * D + col, j0 + row < Skv);
+      vreg[r] = vbuf.ld16((uint32_t)((j0 + row) * D + col) * 2);
     }
   };
 

@@ -57,6 +57,30 @@ __device__ __forceinline__ f32x16 zero_f32x16() {
   return z;
 }
 
+// Range-checked raw buffer access.  The descriptor covers `nbytes` bytes from
+// a wave-uniform base; a load whose offset falls outside returns zero without
+// touching memory, so tile loads over ragged tails need no branches.
+// Descriptor word 3 selects 32-bit data format, the plain gfx9 raw-buffer
+// setting.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct Buf {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ Buf(const void* base, uint32_t nbytes)
+      : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)nbytes,
+                                            0x00020000)) {}
+  __device__ __forceinline__ uint4 ld16(uint32_t off) const {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+  }
+  __device__ __forceinline__ uint32_t ld4(uint32_t off) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  __device__ __forceinline__ float ldf(uint32_t off) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+};
+
 // 16-byte global load of 8 bf16, or zeros when !valid.
 __device__ __forceinline__ uint4 ld16(const bf16* p, bool valid) {
   if (valid) return *reinterpret_cast<const uint4*>(p);
@@ -91,12 +115,29 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
-template <int N>
-__device__ __forceinline__ bf16x8 pack8(const f32x16& v, int base) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (bf16)v[base + e];
-  return r;
+// Workgroup -> (head, query tile) order, assuming round-robin dispatch of
+// consecutive workgroup ids over the 8 XCDs (id % 8 = XCD), each with its own
+// L2.  Non-causal: head-major, remapped so that each XCD walks a contiguous
+// run of tiles (tiles of one head share K/V, which then stays in that XCD's
+// L2).  Causal: longest query tiles first across the whole grid, and inside
+// each tile level each XCD takes a contiguous run of heads, the same run at
+// every level, so grouped query heads and their K/V stay on one XCD.
+__device__ __forceinline__ void tile_of_block(int p, int nbh, int n_qt, bool causal, int& bh,
+                                              int& qt) {
+  if (causal) {
+    const int level = p / nbh, r = p - level * nbh;
+    bh = ((nbh & 7) == 0) ? (r & 7) * (nbh >> 3) + (r >> 3) : r;
+    qt = n_qt - 1 - level;
+  } else {
+    const int N = nbh * n_qt;
+    const int L = ((N & 7) == 0) ? (p & 7) * (N >> 3) + (p >> 3) : p;
+    bh = L / n_qt;
+    qt = L - bh * n_qt;
+  }
+}
+
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
 }
 
 __device__ __forceinline__ float wave_max(float x) {

@@ -52,15 +52,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
 
-  int qt = blockIdx.x % n_qt;
-  const int bh = blockIdx.x / n_qt;
-  if (CAUSAL) qt = n_qt - 1 - qt;  // longest rows first
+  int bh, qt;
+  tile_of_block(blockIdx.x, gridDim.x / n_qt, n_qt, CAUSAL, bh, qt);
   const int h = bh % Hq, b = bh / Hq;
   const int Hkv = Hq / G;
   const size_t kv_off = ((size_t)(b * Hkv + h / G) * Skv) * D;
-  const bf16* Qh = Q + (size_t)bh * Sq * D;
-  const bf16* Kh = K + kv_off;
-  const bf16* Vh = V + kv_off;
+  const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
+  const Buf kbuf(K + kv_off, (uint32_t)Skv * D * 2);
+  const Buf vbuf(V + kv_off, (uint32_t)Skv * D * 2);
 
   const int q0 = qt * FWD_BM;
   const int qw0 = q0 + wave * 32;          // first query of this wave
@@ -71,13 +70,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   bf16x8 qf[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s)
-    qf[s] = as_bf16x8(ld16(Qh + (size_t)qrow * D + 16 * s + 8 * g, qrow < Sq));
+    qf[s] = as_bf16x8(qbuf.ld16((uint32_t)(qrow * D + 16 * s + 8 * g) * 2));
 
   int kv_end = Skv;
   if (CAUSAL) kv_end = min(Skv, q0 + FWD_BM + diag);
   const int n_kt = (kv_end + FWD_BN - 1) / FWD_BN;
 
-  // Register staging of one K/V tile.
+  // Register staging of one K/V tile (rows past Skv load as zeros).
   uint4 kreg[T::K_CHUNKS];
   uint32_t vreg[T::V_PASSES][8];
   const int vc = tid % T::V_TPR, vgrp = tid / T::V_TPR;
@@ -87,7 +86,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int r = 0; r < T::K_CHUNKS; ++r) {
       const int ch = tid + FWD_THREADS * r;
       const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      kreg[r] = ld16(Kh + (size_t)(j0 + row) * D + col, j0 + row < Skv);
+      kreg[r] = kbuf.ld16((uint32_t)((j0 + row) * D + col) * 2);
     }
 #pragma unroll
     for (int p = 0; p < T::V_PASSES; ++p) {
@@ -96,7 +95,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int e = 0; e < 8; ++e) {
         const int pos = pos0 + e;
         const int key = j0 + (pos & ~15) + swz(pos & 15);
-        vreg[p][e] = ld4(Vh + (size_t)key * D + 2 * vc, key < Skv);
+        vreg[p][e] = vbuf.ld4((uint32_t)(key * D + 2 * vc) * 2);
       }
     }
   };
@@ -120,8 +119,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = zero_f32x16();
-  float m = -MATTN_INF;  // running max of t over this query's keys (shared by lane, lane^32)
-  float l = 0.f;         // this lane's partial row sum (relative to m)
+  // Reference max of t = s*c for this query (shared by lane and lane^32) and
+  // this lane's partial row sum relative to it.  The reference only moves
+  // when a tile's max exceeds it by more than RESCALE_SLACK (log2 units), so
+  // most tiles skip the O rescale; p <= 2^RESCALE_SLACK stays well inside
+  // fp32/bf16 range and O / l is unchanged.
+  constexpr float RESCALE_SLACK = 8.0f;
+  float m = -MATTN_INF;
+  float l = 0.f;
 
   if (n_kt > 0) load_tile(0);
   for (int kt = 0; kt < n_kt; ++kt) {
@@ -134,20 +139,19 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     // S^T for two 32-key blocks: lane = query column, regs = keys.
     f32x16 sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero_f32x16();
+    for (int kb = 0; kb < 2; ++kb) sc[kb] = zero_f32x16();
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
+    for (int st = 0; st < D / 16; ++st)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * T::KP + 16 * st + 8 * g]);
-        s = mfma32(a, qf[st], s);
+        sc[kb] = mfma32(a, qf[st], sc[kb]);
       }
-      sc[kb] = s;
-    }
 
-    const bool need_mask = (j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag));
+    const bool fast = !((j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag))) && c > 0.f;
     float mt;
-    if (!need_mask && c > 0.f) {
-      float mx = -MATTN_INF;
+    if (fast) {
+      float mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -169,13 +173,20 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       mt = mx;
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m, mt);
-    const float m_use = (m_new == -MATTN_INF) ? 0.f : m_new;
-    const float alpha = fast_exp2(m - m_use);
-    m = m_new;
+    if (wave_any(mt > m + RESCALE_SLACK)) {
+      const float m_new = fmaxf(m, mt);
+      const float alpha = (m_new == -MATTN_INF) ? 1.f : fast_exp2(m - m_new);
+      m = m_new;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    }
+    const float m_use = (m == -MATTN_INF) ? 0.f : m;
 
     float rs = 0.f;
-    if (!need_mask && c > 0.f) {
+    if (fast) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -194,11 +205,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           rs += p;
         }
     }
-    l = l * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+    l += rs;
 
     bf16x8 pb[2][2];
 #pragma unroll
@@ -210,11 +217,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
     // O^T += V^T P^T.
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int db = 0; db < D / 32; ++db) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(
               &Vt[(db * 32 + l32) * T::VP + kb * 32 + 16 * t + 8 * g]);
           acc[db] = mfma32(a, pb[kb][t], acc[db]);

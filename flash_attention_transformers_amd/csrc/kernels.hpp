@@ -15,7 +15,7 @@ struct Problem {
 // bwd_bf16.hip).  Depends only on the sizes.
 int bwd_nsplit(int B, int Hkv, int Sq, int Skv);
 constexpr int BWD_BN = 128;  // keys per dK/dV workgroup
-constexpr int BWD_BMQ = 32;  // query rows per dK/dV inner step
+constexpr int BWD_BMQ = 64;  // query rows per dK/dV inner step
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v,
                            void* o, float* lse, hipStream_t stream);

@@ -43,7 +43,7 @@ SMALL = [
     wl("one_query", 1, 2, 2, 1, 200, 128, False),
     wl("decode_row_causal", 1, 4, 2, 1, 300, 128, True),
     wl("split_q_chunks", 1, 2, 2, 1000, 257, 128, False),
-    wl("split_q_chunks_gqa", 1, 4, 2, 900, 130, 64, False),
+    wl("split_q_chunks_gqa", 1, 4, 2, 1100, 130, 64, False),
     wl("f32_d64", 1, 2, 2, 128, 128, 64, False, dtype="f32"),
     wl("f32_d128_causal_gqa", 1, 4, 2, 150, 150, 128, True, dtype="f32"),
     wl("f32_ragged_cross", 2, 2, 1, 70, 33, 64, False, dtype="f32"),
