@@ -10,19 +10,27 @@
 //
 // Three kernels on one stream:
 //  1. preprocess: Dlt[row] = sum_d dO[row,d] * O[row,d]            (HBM bound)
-//  2. dK/dV: one workgroup per 128 keys of one KV head; each wave keeps its
-//     32 keys' K and V rows in registers as MFMA B operands and walks the
-//     query tiles of every query head of the group:
-//        S = Q K^T, dP = dO V^T            (lane = key column)
-//        P = 2^(S*scale*log2e - LSE*log2e), dS = P (dP - Dlt)
-//        dV^T += dO^T P,  dK^T += Q^T dS   (P, dS fed from registers)
-//     Shapes with few KV tiles (short cross-attention KV) split the query
-//     range into fixed chunks that write fp32 partials, summed afterwards in
-//     chunk order by a reduction kernel.
+//  2. dK/dV: one workgroup per 128 keys of one KV head, 8 waves: four
+//     32-key slices, each served by a pair of waves with split roles so that
+//     each wave fits in half a SIMD's registers and two waves share a SIMD:
+//       P-wave : S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e)  -> P to LDS,
+//                dV^T += dO^T P
+//       dS-wave: dP = dO V^T, dS = P (dP - Dlt) with P from LDS,
+//                dK^T += Q^T dS
+//     (lane = key column; K or V of the slice stays in registers as the MFMA
+//     B operand).  The walk covers every query tile of every query head of
+//     the group, in ascending head order, summing in registers.  Shapes with
+//     few KV tiles (short cross-attention KV) split the query range into
+//     fixed chunks that write fp32 partials, summed afterwards in chunk order
+//     by a reduction kernel.
 //  3. dQ: one workgroup per 128 query rows; each wave keeps its 32 rows of Q
 //     and dO in registers and walks the K/V tiles:
 //        S^T = K Q^T, dP^T = V dO^T        (lane = query column)
 //        dQ^T += K^T dS^T
+// Q/dO and K/V tiles are staged row-major in LDS; every transposed MFMA
+// operand (dO^T, Q^T, K^T) is read with ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -68,40 +76,12 @@ void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
 }
 
 // ----------------------------------------------------------------------------
-// Load 8 rows x 2 columns of a [rows x D] bf16 tile with 4-byte buffer loads
-// (rows past the descriptor's range read as zero) and write it to LDS twice:
-// row-major (pitch NP) and transposed with the swz row order (pitch TP).
-// `pos0` is the first (multiple-of-8) transposed position; the rows it covers
-// are (pos & ~15) + swz(pos & 15).
-template <int D, int NP, int TP>
-struct DualTile {
-  uint32_t w[8];
-  __device__ __forceinline__ void load(const Buf& src, int row0, int pos0, int c2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pos = pos0 + e;
-      const int r = (pos & ~15) + swz(pos & 15);
-      w[e] = src.ld4((uint32_t)((row0 + r) * D + 2 * c2) * 2);
-    }
-  }
-  __device__ __forceinline__ void store(bf16* nat, bf16* tr, int pos0, int c2) const {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int pos = pos0 + e;
-      const int r = (pos & ~15) + swz(pos & 15);
-      *reinterpret_cast<uint32_t*>(&nat[r * NP + 2 * c2]) = w[e];
-    }
-    uint4 lo, hi;
-    split_pairs(w, lo, hi);
-    *reinterpret_cast<uint4*>(&tr[(2 * c2) * TP + pos0]) = lo;
-    *reinterpret_cast<uint4*>(&tr[(2 * c2 + 1) * TP + pos0]) = hi;
-  }
-};
-
 // ----------------------------------------------------------------------------
 // 2. dK/dV
+constexpr int DKDV_THREADS = 512;  // 4 key slices x 2 roles
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(THREADS, 1)
+__global__ __launch_bounds__(DKDV_THREADS)
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, const bf16* __restrict__ dO,
                      const float* __restrict__ LSE, const float* __restrict__ DLT,
@@ -110,21 +90,20 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      int nsplit, int q_chunk) {
   constexpr int BMQ = BWD_BMQ;            // query rows per step (two 32-row sub-blocks)
   constexpr int NSUB = BMQ / 32;
-  constexpr int NP = D + 8;
-  constexpr int TP = BMQ + 8;
-  constexpr int LTPR = D / 2;             // loader threads per 8-row group (2 columns each)
-  constexpr int LGROUPS = BMQ / 8;
-  constexpr int LPASSES = LTPR * LGROUPS / THREADS;
-  static_assert((LTPR * LGROUPS) % THREADS == 0, "tile loader must tile the workgroup");
-  __shared__ __attribute__((aligned(16))) bf16 Qs[BMQ * NP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[BMQ * NP];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[D * TP];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[D * TP];
+  constexpr int P = TilePitch<D>::value;
+  constexpr int CH = BMQ * D / 8 / DKDV_THREADS;  // 16-byte chunks per thread per tensor
+  static_assert(CH >= 1 && (BMQ * D / 8) % DKDV_THREADS == 0, "tile loader must tile the workgroup");
+  __shared__ __attribute__((aligned(16))) bf16 Qs[BMQ * P];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[BMQ * P];
+  // P handed from each P-wave to its dS-wave: [slice][sub-block][blk][lane][4].
+  __shared__ __attribute__((aligned(16))) float Pex[4 * NSUB * 4 * 64 * 4];
   __shared__ __attribute__((aligned(16))) float lse_s[BMQ];
   __shared__ __attribute__((aligned(16))) float dlt_s[BMQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
+  const int slice = wave & 3;
+  const bool pwave = wave < 4;
   const int Hkv = Hq / G;
 
   const int split = blockIdx.x % nsplit;
@@ -133,25 +112,20 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int bkv = rest / n_kt;
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int k0 = kt * BWD_BN;
-  const int kw0 = k0 + wave * 32;
+  const int kw0 = k0 + slice * 32;
   const int key = kw0 + l32;
   const int diag = Skv - Sq;
 
+  // The P-wave keeps K of its slice, the dS-wave keeps V, as MFMA B operands.
   const size_t kv_off = (size_t)bkv * Skv * D;
-  const Buf kbuf(K + kv_off, (uint32_t)Skv * D * 2);
-  const Buf vbuf(V + kv_off, (uint32_t)Skv * D * 2);
-  bf16x8 kf[D / 16], vf[D / 16];
+  const Buf kvbuf(pwave ? K + kv_off : V + kv_off, (uint32_t)Skv * D * 2);
+  bf16x8 kvf[D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    kf[s] = as_bf16x8(kbuf.ld16((uint32_t)(key * D + 16 * s + 8 * g) * 2));
-    vf[s] = as_bf16x8(vbuf.ld16((uint32_t)(key * D + 16 * s + 8 * g) * 2));
-  }
-  f32x16 adk[D / 32], adv[D / 32];
+  for (int st = 0; st < D / 16; ++st)
+    kvf[st] = as_bf16x8(kvbuf.ld16((uint32_t)(key * D + 16 * st + 8 * g) * 2));
+  f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave)
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) {
-    adk[db] = zero_f32x16();
-    adv[db] = zero_f32x16();
-  }
+  for (int db = 0; db < D / 32; ++db) acc[db] = zero_f32x16();
 
   // Query range of this chunk (q_chunk is a multiple of BMQ).
   const int qs = split * q_chunk;
@@ -164,9 +138,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int nq = qe > q_lo ? (qe - q_lo + BMQ - 1) / BMQ : 0;
   const int n_it = G * nq;
 
-  DualTile<D, NP, TP> tq[LPASSES], tdo[LPASSES];
+  uint4 qreg[CH], doreg[CH];
   float pre_lse = 0.f, pre_dlt = 0.f;
-
   auto load_it = [&](int it) {
     const int r = it / nq, qi = it - r * nq;
     const int h = kvh * G + r;
@@ -176,14 +149,15 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const Buf qbuf(Q + hoff * D, (uint32_t)Sq * D * 2);
     const Buf dobuf(dO + hoff * D, (uint32_t)Sq * D * 2);
 #pragma unroll
-    for (int ps = 0; ps < LPASSES; ++ps) {
-      const int lt = tid + ps * THREADS;
-      tq[ps].load(qbuf, qt0, 8 * (lt / LTPR), lt % LTPR);
-      tdo[ps].load(dobuf, qt0, 8 * (lt / LTPR), lt % LTPR);
+    for (int r2 = 0; r2 < CH; ++r2) {
+      const int ch = tid + DKDV_THREADS * r2;
+      const uint32_t off = (uint32_t)((qt0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2;
+      qreg[r2] = qbuf.ld16(off);
+      doreg[r2] = dobuf.ld16(off);
     }
+    const Buf lbuf(LSE + hoff, (uint32_t)Sq * 4);
+    const Buf dbuf(DLT + hoff, (uint32_t)Sq * 4);
     if (tid < BMQ) {
-      const Buf lbuf(LSE + hoff, (uint32_t)Sq * 4);
-      const Buf dbuf(DLT + hoff, (uint32_t)Sq * 4);
       pre_lse = lbuf.ldf((uint32_t)(qt0 + tid) * 4);
       pre_dlt = dbuf.ldf((uint32_t)(qt0 + tid) * 4);
     }
@@ -194,10 +168,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int qt0 = q_lo + (it % nq) * BMQ;
     __syncthreads();
 #pragma unroll
-    for (int ps = 0; ps < LPASSES; ++ps) {
-      const int lt = tid + ps * THREADS;
-      tq[ps].store(Qs, Qt, 8 * (lt / LTPR), lt % LTPR);
-      tdo[ps].store(dOs, dOt, 8 * (lt / LTPR), lt % LTPR);
+    for (int r2 = 0; r2 < CH; ++r2) {
+      const int ch = tid + DKDV_THREADS * r2;
+      const int o = (ch / (D / 8)) * P + (ch % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Qs[o]) = qreg[r2];
+      *reinterpret_cast<uint4*>(&dOs[o]) = doreg[r2];
     }
     if (tid < BMQ) {
       // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
@@ -208,94 +183,104 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     __syncthreads();
     if (it + 1 < n_it) load_it(it + 1);
 
-    // S = Q K^T and dP = dO V^T per 32-row sub-block: lane = key column,
-    // regs = query rows.
-    f32x16 s[NSUB], dp[NSUB];
-#pragma unroll
-    for (int qb = 0; qb < NSUB; ++qb) {
-      s[qb] = zero_f32x16();
-      dp[qb] = zero_f32x16();
-    }
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st)
+    const bool masked = CAUSAL && (kw0 + 31 > qt0 + diag);
+    float* pex = Pex + slice * (NSUB * 4 * 64 * 4);
+    if (pwave) {
+      // S = Q K^T (lane = key column, regs = query rows) -> P.
+      bf16x8 pb[NSUB][2];
 #pragma unroll
       for (int qb = 0; qb < NSUB; ++qb) {
-        const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[(qb * 32 + l32) * NP + 16 * st + 8 * g]);
-        const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dOs[(qb * 32 + l32) * NP + 16 * st + 8 * g]);
-        s[qb] = mfma32(aq, kf[st], s[qb]);
-        dp[qb] = mfma32(ad, vf[st], dp[qb]);
-      }
-    const bool need_mask = CAUSAL && (kw0 + 31 > qt0 + diag);
-    bf16x8 pb[NSUB][2], dsb[NSUB][2];
+        f32x16 sa = zero_f32x16();
 #pragma unroll
-    for (int qb = 0; qb < NSUB; ++qb) {
+        for (int st = 0; st < D / 16; ++st)
+          sa = mfma32(ld_row_operand(Qs, P, qb * 32, 16 * st, lane), kvf[st], sa);
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const f32x4 L = *reinterpret_cast<const f32x4*>(&lse_s[qb * 32 + 8 * blk + 4 * g]);
-        const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[qb * 32 + 8 * blk + 4 * g]);
+        for (int blk = 0; blk < 4; ++blk) {
+          const f32x4 L = *reinterpret_cast<const f32x4*>(&lse_s[qb * 32 + 8 * blk + 4 * g]);
+          f32x4 pv;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = 4 * blk + j;
-          float p = fast_exp2(__builtin_fmaf(s[qb][i], c, -L[j]));
-          if (need_mask && key > qt0 + qb * 32 + crow(i, g) + diag) p = 0.f;
-          s[qb][i] = p;
-          dp[qb][i] = p * (dp[qb][i] - Dl[j]);
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * blk + j;
+            float pr = fast_exp2(__builtin_fmaf(sa[i], c, -L[j]));
+            if (masked && key > qt0 + qb * 32 + crow(i, g) + diag) pr = 0.f;
+            pv[j] = pr;
+            pb[qb][i >> 3][i & 7] = (bf16)pr;
+          }
+          *reinterpret_cast<f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]) = pv;
         }
       }
+      __syncthreads();
+      // dV^T += dO^T P.
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int qb = 0; qb < NSUB; ++qb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[qb][t][e] = (bf16)s[qb][8 * t + e];
-          dsb[qb][t][e] = (bf16)dp[qb][8 * t + e];
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            acc[db] = mfma32(ld_trans_operand(dOs, P, qb * 32 + 16 * t, db * 32, lane),
+                             pb[qb][t], acc[db]);
+    } else {
+      // dP = dO V^T, same layout as S.
+      f32x16 dp[NSUB];
+#pragma unroll
+      for (int qb = 0; qb < NSUB; ++qb) {
+        dp[qb] = zero_f32x16();
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st)
+          dp[qb] = mfma32(ld_row_operand(dOs, P, qb * 32, 16 * st, lane), kvf[st], dp[qb]);
+      }
+      __syncthreads();
+      // dS = P (dP - Dlt); dK^T += Q^T dS.
+#pragma unroll
+      for (int qb = 0; qb < NSUB; ++qb) {
+        bf16x8 dsb[2];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[qb * 32 + 8 * blk + 4 * g]);
+          const f32x4 pv = *reinterpret_cast<const f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = 4 * blk + j;
+            dsb[i >> 3][i & 7] = (bf16)(pv[j] * (dp[qb][i] - Dl[j]));
+          }
         }
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            acc[db] = mfma32(ld_trans_operand(Qs, P, qb * 32 + 16 * t, db * 32, lane),
+                             dsb[t], acc[db]);
+      }
     }
-    // dV^T += dO^T P, dK^T += Q^T dS.
-#pragma unroll
-    for (int qb = 0; qb < NSUB; ++qb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const int col = qb * 32 + 16 * t + 8 * g;
-          const bf16x8 ado = *reinterpret_cast<const bf16x8*>(&dOt[(db * 32 + l32) * TP + col]);
-          const bf16x8 aqt = *reinterpret_cast<const bf16x8*>(&Qt[(db * 32 + l32) * TP + col]);
-          adv[db] = mfma32(ado, pb[qb][t], adv[db]);
-          adk[db] = mfma32(aqt, dsb[qb][t], adk[db]);
-        }
   }
 
   if (key >= Skv) return;
+  const float mul = pwave ? 1.f : scale;  // dK = scale * Q^T dS
   if (nsplit == 1) {
-    bf16* pk = dK + kv_off + (size_t)key * D;
-    bf16* pv = dV + kv_off + (size_t)key * D;
+    bf16* pout = (pwave ? dV : dK) + kv_off + (size_t)key * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int d = db * 32 + r * 8 + g * 4;
-        uint2 wk, wv;
-        wk.x = pack_bf16x2(adk[db][4 * r] * scale, adk[db][4 * r + 1] * scale);
-        wk.y = pack_bf16x2(adk[db][4 * r + 2] * scale, adk[db][4 * r + 3] * scale);
-        wv.x = pack_bf16x2(adv[db][4 * r], adv[db][4 * r + 1]);
-        wv.y = pack_bf16x2(adv[db][4 * r + 2], adv[db][4 * r + 3]);
-        *reinterpret_cast<uint2*>(pk + d) = wk;
-        *reinterpret_cast<uint2*>(pv + d) = wv;
+        uint2 w;
+        w.x = pack_bf16x2(acc[db][4 * r] * mul, acc[db][4 * r + 1] * mul);
+        w.y = pack_bf16x2(acc[db][4 * r + 2] * mul, acc[db][4 * r + 3] * mul);
+        *reinterpret_cast<uint2*>(pout + d) = w;
       }
   } else {
-    // fp32 partials: [2][nsplit][B*Hkv][n_kt*BWD_BN][D]
+    // fp32 partials, unscaled: [dK, dV][nsplit][B*Hkv][n_kt*BWD_BN][D]
     const size_t rows_all = (size_t)(gridDim.x / nsplit / n_kt) * n_kt * BWD_BN;
     const size_t half = (size_t)nsplit * rows_all * D;
-    const size_t ro = ((size_t)split * rows_all + (size_t)bkv * n_kt * BWD_BN + key) * D;
+    const size_t ro = (pwave ? half : 0) +
+                      ((size_t)split * rows_all + (size_t)bkv * n_kt * BWD_BN + key) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int d = db * 32 + r * 8 + g * 4;
         *reinterpret_cast<f32x4*>(part + ro + d) =
-            f32x4{adk[db][4 * r], adk[db][4 * r + 1], adk[db][4 * r + 2], adk[db][4 * r + 3]};
-        *reinterpret_cast<f32x4*>(part + half + ro + d) =
-            f32x4{adv[db][4 * r], adv[db][4 * r + 1], adv[db][4 * r + 2], adv[db][4 * r + 3]};
+            f32x4{acc[db][4 * r], acc[db][4 * r + 1], acc[db][4 * r + 2], acc[db][4 * r + 3]};
       }
   }
 }
@@ -341,16 +326,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const float* __restrict__ LSE, const float* __restrict__ DLT,
                    bf16* __restrict__ dQ, int Hq, int G, int Sq, int Skv, float scale, float c,
                    int n_qt) {
-  constexpr int NP = D + 8;
-  constexpr int TP = DQ_BN + 8;
-  constexpr int LTPR = D / 2;
-  constexpr int LGROUPS = DQ_BN / 8;
-  constexpr int LPASSES = (LTPR * LGROUPS + THREADS - 1) / THREADS;
-  static_assert((LTPR * LGROUPS) % THREADS == 0, "K loader must tile the workgroup exactly");
-  constexpr int V_CHUNKS = DQ_BN * D / 8 / THREADS;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[DQ_BN * NP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[DQ_BN * NP];
-  __shared__ __attribute__((aligned(16))) bf16 Kt[D * TP];
+  constexpr int P = TilePitch<D>::value;
+  constexpr int CH = DQ_BN * D / 8 / THREADS;  // 16-byte chunks per thread per tensor
+  __shared__ __attribute__((aligned(16))) bf16 Ks[DQ_BN * P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[DQ_BN * P];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -383,19 +362,14 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   if (CAUSAL) kv_end = min(Skv, q0 + DQ_BM + diag);
   const int n_kt = (kv_end + DQ_BN - 1) / DQ_BN;
 
-  DualTile<D, NP, TP> tk[LPASSES];
-  uint4 vreg[V_CHUNKS];
+  uint4 kreg[CH], vreg[CH];
   auto load_tile = [&](int j0) {
 #pragma unroll
-    for (int ps = 0; ps < LPASSES; ++ps) {
-      const int lt = tid + ps * THREADS;
-      tk[ps].load(kbuf, j0, 8 * (lt / LTPR), lt % LTPR);
-    }
-#pragma unroll
-    for (int r = 0; r < V_CHUNKS; ++r) {
+    for (int r = 0; r < CH; ++r) {
       const int ch = tid + THREADS * r;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      vreg[r] = vbuf.ld16((uint32_t)((j0 + row) * D + col) * 2);
+      const uint32_t off = (uint32_t)((j0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2;
+      kreg[r] = kbuf.ld16(off);
+      vreg[r] = vbuf.ld16(off);
     }
   };
 
@@ -408,55 +382,48 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int j0 = kt * DQ_BN;
     __syncthreads();
 #pragma unroll
-    for (int ps = 0; ps < LPASSES; ++ps) {
-      const int lt = tid + ps * THREADS;
-      tk[ps].store(Ks, Kt, 8 * (lt / LTPR), lt % LTPR);
-    }
-#pragma unroll
-    for (int r = 0; r < V_CHUNKS; ++r) {
+    for (int r = 0; r < CH; ++r) {
       const int ch = tid + THREADS * r;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Vs[row * NP + col]) = vreg[r];
+      const int o = (ch / (D / 8)) * P + (ch % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Ks[o]) = kreg[r];
+      *reinterpret_cast<uint4*>(&Vs[o]) = vreg[r];
     }
     __syncthreads();
     if (kt + 1 < n_kt) load_tile(j0 + DQ_BN);
 
-    const bool need_mask = (j0 + DQ_BN > Skv) || (CAUSAL && (j0 + DQ_BN - 1 > qw0 + diag));
-    bf16x8 dsb[2][2];
+    auto step = [&](auto masked) {
+      constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * NP + 16 * st + 8 * g]);
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[(kb * 32 + l32) * NP + 16 * st + 8 * g]);
-        s = mfma32(ak, qf[st], s);
-        dp = mfma32(av, dof[st], dp);
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float p = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
-        if (need_mask) {
-          const int kk = j0 + kb * 32 + crow(i, g);
-          if (kk >= Skv || (CAUSAL && kk > qrow + diag)) p = 0.f;
+        for (int st = 0; st < D / 16; ++st) {
+          s = mfma32(ld_row_operand(Ks, P, kb * 32, 16 * st, lane), qf[st], s);
+          dp = mfma32(ld_row_operand(Vs, P, kb * 32, 16 * st, lane), dof[st], dp);
         }
-        s[i] = p * (dp[i] - dl);
-      }
+        bf16x8 dsb[2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dsb[kb][t][e] = (bf16)s[8 * t + e];
-    }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Kt[(db * 32 + l32) * TP + kb * 32 + 16 * t + 8 * g]);
-          adq[db] = mfma32(a, dsb[kb][t], adq[db]);
+        for (int i = 0; i < 16; ++i) {
+          float p = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
+          if (MASK) {
+            const int kk = j0 + kb * 32 + crow(i, g);
+            if (kk >= Skv || (CAUSAL && kk > qrow + diag)) p = 0.f;
+          }
+          dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dl));
         }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db)
+            adq[db] = mfma32(ld_trans_operand(Ks, P, kb * 32 + 16 * t, db * 32, lane), dsb[t],
+                             adq[db]);
+      }
+    };
+    if ((j0 + DQ_BN > Skv) || (CAUSAL && (j0 + DQ_BN - 1 > qw0 + diag)))
+      step(std::true_type{});
+    else
+      step(std::false_type{});
   }
 
   if (qrow < Sq) {
@@ -501,7 +468,7 @@ hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const vo
   const int n_qt32 = (p.Sq + BWD_BMQ - 1) / BWD_BMQ;
   const int q_chunk = ((n_qt32 + nsplit - 1) / nsplit) * BWD_BMQ;
   const long long blocks = (long long)p.B * p.Hkv * n_kt * nsplit;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(THREADS), 0,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(DKDV_THREADS), 0,
                      stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                      lse, dlt, (bf16*)dk, (bf16*)dv, part, p.Hq, G, p.Sq, p.Skv, p.scale, c,
                      n_kt, nsplit, q_chunk);

@@ -41,6 +41,41 @@ __device__ __forceinline__ constexpr int crow(int i, int g) {
   return (i >> 2) * 8 + g * 4 + (i & 3);
 }
 
+// A operand of mfma32 holding the TRANSPOSE of a row-major bf16 tile in LDS:
+// operand row r (lane row l32) is tile column col0 + r, and k-slot 8g + e of
+// the k-step is tile row row0 + swz(8g + e), the order in which a C tile fed
+// as the B operand carries its rows.  Built from two ds_read_b64_tr_b16: in
+// each 16-lane group that instruction hands lane i element (i % 4) of the
+// 8-byte chunk read by source lane 4e + i/4, so source lane s of group j reads
+// tile row row0 + 8h + 4(j/2) + s/4 at columns col0 + 16(j%2) + 4(s%4) .. +3.
+// `pitch` (elements) must be a multiple of 4.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 ld_trans_operand(const bf16* tile, int pitch, int row0,
+                                                   int col0, int lane) {
+  const int j = lane >> 4, s = lane & 15;
+  const bf16* p = tile + (row0 + 4 * (j >> 1) + (s >> 2)) * pitch + col0 + 16 * (j & 1) + 4 * (s & 3);
+  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * pitch));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// A operand of mfma32 read straight from a row-major bf16 tile in LDS:
+// lane row l32 = tile row row0 + l32, k-slots 8g..8g+7 = columns col0 + 8g ...
+__device__ __forceinline__ bf16x8 ld_row_operand(const bf16* tile, int pitch, int row0, int col0,
+                                                 int lane) {
+  return *reinterpret_cast<const bf16x8*>(&tile[(row0 + (lane & 31)) * pitch + col0 + 8 * (lane >> 5)]);
+}
+
+// LDS row pitch (bf16 elements) for [rows x D] tiles read both by rows (16 B
+// per lane, 16 consecutive rows) and by ld_trans_operand (4 consecutive rows,
+// 32 B each): with 64 four-byte banks both patterns hit distinct banks when
+// the pitch is 304 B (D = 128) or 208 B (D = 64).
+template <int D>
+struct TilePitch {
+  static constexpr int value = D == 128 ? 152 : 104;
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ bf16x8 zero_bf16x8() {

@@ -9,9 +9,11 @@
 // Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
 //  * each wave owns 32 query rows and keeps them as the B operand of
 //    S^T = K Q^T in registers for the whole kernel (lane = query column);
-//  * K/V tiles of 64 keys are staged through LDS: K row-major (the A operand
-//    of S^T), V transposed with the swz key order (the A operand of
-//    O^T = V^T P^T), prefetched into registers one tile ahead;
+//  * K/V tiles of 64 keys are staged row-major through LDS (16-byte buffer
+//    loads, prefetched into registers one tile ahead); K rows are the A
+//    operand of S^T, and the A operand of O^T = V^T P^T is read transposed
+//    straight from the V tile with ds_read_b64_tr_b16, in the key order that
+//    P^T carries out of the S^T accumulator;
 //  * S^T lands with one query per lane, so the running row max and row sum
 //    are per-lane scalars: 32 in-lane values plus one exchange with lane^32;
 //  * P is rounded to bf16 and fed to the PV MFMA straight from registers;
@@ -31,12 +33,8 @@ constexpr int FWD_THREADS = 256;
 
 template <int D>
 struct FwdTile {
-  static constexpr int KP = D + 8;        // K row pitch in LDS (bf16)
-  static constexpr int VP = FWD_BN + 8;   // V^T row pitch in LDS (bf16)
-  static constexpr int K_CHUNKS = FWD_BN * D / 8 / FWD_THREADS;  // 16-byte chunks per thread
-  static constexpr int V_TPR = D / 2;                     // threads per key row (2 columns each)
-  static constexpr int V_GROUPS = FWD_THREADS / V_TPR;    // 8-key groups per pass
-  static constexpr int V_PASSES = FWD_BN / (8 * V_GROUPS);
+  static constexpr int P = TilePitch<D>::value;                  // LDS row pitch (bf16)
+  static constexpr int CHUNKS = FWD_BN * D / 8 / FWD_THREADS;    // 16-byte chunks per thread per tensor
 };
 
 template <int D, bool CAUSAL>
@@ -46,8 +44,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      float* __restrict__ LSE, int Hq, int G, int Sq, int Skv,
                      float c /* scale*log2(e) */, int n_qt) {
   using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * T::KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[D * T::VP];
+  __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * T::P];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[FWD_BN * T::P];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -77,42 +75,23 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int n_kt = (kv_end + FWD_BN - 1) / FWD_BN;
 
   // Register staging of one K/V tile (rows past Skv load as zeros).
-  uint4 kreg[T::K_CHUNKS];
-  uint32_t vreg[T::V_PASSES][8];
-  const int vc = tid % T::V_TPR, vgrp = tid / T::V_TPR;
-
+  uint4 kreg[T::CHUNKS], vreg[T::CHUNKS];
   auto load_tile = [&](int j0) {
 #pragma unroll
-    for (int r = 0; r < T::K_CHUNKS; ++r) {
+    for (int r = 0; r < T::CHUNKS; ++r) {
       const int ch = tid + FWD_THREADS * r;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      kreg[r] = kbuf.ld16((uint32_t)((j0 + row) * D + col) * 2);
-    }
-#pragma unroll
-    for (int p = 0; p < T::V_PASSES; ++p) {
-      const int pos0 = 8 * (p * T::V_GROUPS + vgrp);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int pos = pos0 + e;
-        const int key = j0 + (pos & ~15) + swz(pos & 15);
-        vreg[p][e] = vbuf.ld4((uint32_t)(key * D + 2 * vc) * 2);
-      }
+      const uint32_t off = (uint32_t)((j0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2;
+      kreg[r] = kbuf.ld16(off);
+      vreg[r] = vbuf.ld16(off);
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
-    for (int r = 0; r < T::K_CHUNKS; ++r) {
+    for (int r = 0; r < T::CHUNKS; ++r) {
       const int ch = tid + FWD_THREADS * r;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Ks[row * T::KP + col]) = kreg[r];
-    }
-#pragma unroll
-    for (int p = 0; p < T::V_PASSES; ++p) {
-      const int pos0 = 8 * (p * T::V_GROUPS + vgrp);
-      uint4 lo, hi;
-      split_pairs(vreg[p], lo, hi);
-      *reinterpret_cast<uint4*>(&Vt[(2 * vc) * T::VP + pos0]) = lo;
-      *reinterpret_cast<uint4*>(&Vt[(2 * vc + 1) * T::VP + pos0]) = hi;
+      const int o = (ch / (D / 8)) * T::P + (ch % (D / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Ks[o]) = kreg[r];
+      *reinterpret_cast<uint4*>(&Vs[o]) = vreg[r];
     }
   };
 
@@ -144,8 +123,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int st = 0; st < D / 16; ++st)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(kb * 32 + l32) * T::KP + 16 * st + 8 * g]);
-        sc[kb] = mfma32(a, qf[st], sc[kb]);
+        sc[kb] = mfma32(ld_row_operand(Ks, T::P, kb * 32, 16 * st, lane), qf[st], sc[kb]);
       }
 
     const bool fast = !((j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag))) && c > 0.f;
@@ -222,9 +200,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &Vt[(db * 32 + l32) * T::VP + kb * 32 + 16 * t + 8 * g]);
-          acc[db] = mfma32(a, pb[kb][t], acc[db]);
+          acc[db] = mfma32(ld_trans_operand(Vs, T::P, kb * 32 + 16 * t, db * 32, lane),
+                           pb[kb][t], acc[db]);
         }
   }
 
