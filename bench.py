@@ -1,16 +1,26 @@
 """Benchmark of the fused attention hot path on one MI355X.
 
-One step = mattn_fwd + mattn_bwd (forward kernel, D = sum(dO*O) preprocess,
-dK/dV kernel, dQ kernel) over one batch of seeded synthetic input that is
-already resident in HBM.  Default workload: GQA causal training attention,
-B=4, Hq=32, Hkv=8, S=4096, D=128, bf16 (the long-sequence configuration that
-exercises every step of the path, including the grouped-KV head map and the
-group-summed backward).
+One step = mattn_fwd + the backward (D = sum(dO*O) preprocess, dK/dV kernel,
+dQ kernel) over one batch of seeded synthetic input that is already resident
+in HBM.  The backward is enqueued as its three stages (mattn_bwd_stages, the
+same kernels mattn_bwd issues, in the same order on the same stream) so that
+HIP events between them time each kernel inside the timed region.
+
+Default workload: GQA causal training attention, B=4, Hq=32, Hkv=8, S=4096,
+D=128, bf16 (the long-sequence configuration that exercises every step of the
+path, including the grouped-KV head map and the group-summed backward).
 
 Prints ONE JSON line.  `value` is credited TFLOP/s of the whole step:
 (4*B*Hq*Sq*Skv*D forward + 2.5x that backward, halved for causal) / step time.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --copy-probe   # plain 1 GiB device copy, to calibrate HBM byte counters
+
+The roofline object describes the kernel with the largest share of the step.
+Algorithmic work per launch, with F = 4*B*Hq*Sq*Skv*D (halved when causal):
+forward F (QK^T and PV); dK/dV 2F (S, dP, dV, dK); dQ 1.5F (S, dP, dQ).  The
+two backward kernels each recompute S and dP, so together they execute 3.5F
+against the 2.5F credited to the backward.
 """
 from __future__ import annotations
 
@@ -30,25 +40,51 @@ F32_PEAK_TFLOPS = 157.3    # MI355X fp32 matrix / packed vector peak
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def _sha(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": "fwd_bf16.hip", "bwd_dkdv_kernel": "bwd_bf16.hip",
+    "bwd_dq_kernel": "bwd_bf16.hip", "fwd_f32_kernel": "attn_f32.hip",
+    "dkdv_f32_kernel": "attn_f32.hip", "dq_f32_kernel": "attn_f32.hip",
+}
 
 
-def _traffic_from_profile(workload: str):
-    """Per-launch HBM bytes of the forward kernel from the committed rocprofv3
-    counter summary, or None if absent or if the kernel source changed since
-    the counters were taken."""
-    path = os.path.join(PROFILES, f"fwd_bf16_kernel_{workload}_hbm_counters.md")
+def _traffic_from_profile(kernel: str, workload: str):
+    """Per-launch HBM bytes of `kernel` from the committed rocprofv3 counter
+    summary, or None if absent or if the kernel's source (or the shared
+    header) changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
     m_b = re.search(r"HBM bytes per launch \(calibrated\): ([0-9.eE+]+)", text)
-    src = os.path.join(ROOT, "flash_attention_transformers_amd", "csrc", "fwd_bf16.hip")
-    if not m_sha or not m_b or m_sha.group(1) != _sha(src):
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_sha(kernel):
         return None
     return float(m_b.group(1))
+
+
+def kernel_source_sha(kernel: str) -> str:
+    csrc = os.path.join(ROOT, "flash_attention_transformers_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "common.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def copy_probe(steps: int):
+    """Plain device-to-device copy of 1 GiB, `steps` times: the reference for
+    scaling FETCH_SIZE / WRITE_SIZE (each launch reads and writes 1 GiB)."""
+    import torch
+
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": steps}), flush=True)
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -103,7 +139,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_causal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-probe", action="store_true", help="run the HBM calibration copy")
     args = ap.parse_args()
+    if args.copy_probe:
+        copy_probe(max(args.steps, 1))
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(attention heads shard across GPUs with no change to the kernel).", file=sys.stderr)
@@ -127,21 +167,25 @@ def main():
     ws = fa.bwd_workspace(q, k)
     stream = torch.cuda.current_stream(dev)
 
+    stages = [fa.MATTN_BWD_PREPROCESS, fa.MATTN_BWD_DKDV, fa.MATTN_BWD_DQ] if w.backward else []
+    names = ["fwd", "pre", "dkdv", "dq"][: 1 + len(stages)]
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
         fa.mattn_fwd(q, k, v, o, lse, w.causal, w.scale, stream)
         if ev is not None:
             ev[1].record(stream)
-        if w.backward:
-            fa.mattn_bwd(q, k, v, o, lse, do, dq, dk, dv, ws, w.causal, w.scale, stream)
-        if ev is not None:
-            ev[2].record(stream)
+        for i, st in enumerate(stages):
+            fa.mattn_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, ws, st, w.causal, w.scale, stream)
+            if ev is not None:
+                ev[2 + i].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    nev = 2 + len(stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -154,8 +198,10 @@ def main():
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps if w.backward else 0.0
+    kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+               for i, n in enumerate(names)}
+    fwd_ms = kern_ms["fwd"]
+    bwd_ms = sum(kern_ms[n] for n in names[1:])
 
     fwd_flop = w.fwd_flop()
     step_flop = fwd_flop + (w.bwd_flop() if w.backward else 0.0)
@@ -164,6 +210,24 @@ def main():
     fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
     bwd_tf = w.bwd_flop() / (bwd_ms * 1e-3) / 1e12 if w.backward else None
 
+    # Roofline of the kernel with the largest share of the step.
+    F = fwd_flop
+    per_launch = {"fwd": F, "dkdv": 2.0 * F, "dq": 1.5 * F}
+    dom = max((n for n in names if n in per_launch), key=lambda n: kern_ms[n])
+    kname = {"fwd": "fwd", "dkdv": "bwd_dkdv", "dq": "bwd_dq"}[dom] + "_kernel"
+    if w.dtype != "bf16":
+        kname = {"fwd": "fwd_f32_kernel", "dkdv": "dkdv_f32_kernel", "dq": "dq_f32_kernel"}[dom]
+    achieved = per_launch[dom] / (kern_ms[dom] * 1e-3) / 1e12
+    roofline = {
+        "kernel": kname,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": _traffic_from_profile(kname, w.name),
+        "flop_per_launch": per_launch[dom],
+    }
     line = {
         "metric": "attention TFLOPS fwd and fwd+bwd at 1 MI355X; % of bf16 MFMA peak",
         "value": round(value, 2),
@@ -190,15 +254,8 @@ def main():
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
         "wall_s_timed_region": round(wall, 4),
-        "roofline": {
-            "kernel": "fwd_bf16_kernel" if w.dtype == "bf16" else "fwd_f32_kernel",
-            "bound": "mfma",
-            "achieved": round(fwd_tf, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(fwd_tf / peak, 4),
-            "traffic": _traffic_from_profile(w.name),
-        },
+        "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+        "roofline": roofline,
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w)

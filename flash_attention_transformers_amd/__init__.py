@@ -23,6 +23,8 @@ LIB_PATH = os.path.join(_HERE, "libmattn.so")
 
 MATTN_OK, MATTN_ERR_INVALID_ARG, MATTN_ERR_UNSUPPORTED, MATTN_ERR_LAUNCH = 0, 1, 2, 3
 MATTN_BF16, MATTN_F32 = 0, 1
+MATTN_BWD_PREPROCESS, MATTN_BWD_DKDV, MATTN_BWD_DQ = 1, 2, 4
+MATTN_BWD_ALL = MATTN_BWD_PREPROCESS | MATTN_BWD_DKDV | MATTN_BWD_DQ
 
 _lib = None
 
@@ -47,6 +49,9 @@ def load_library() -> ctypes.CDLL:
     lib.mattn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i,
                               vp, sz, vp]
     lib.mattn_bwd.restype = i
+    lib.mattn_bwd_stages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                     i, vp, sz, ctypes.c_uint, vp]
+    lib.mattn_bwd_stages.restype = i
     lib.mattn_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.mattn_bwd_workspace_size.restype = sz
     lib.mattn_strerror.argtypes = [i]
@@ -135,6 +140,24 @@ def mattn_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,
                                   dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D, int(causal),
                                   float(scale), _dtype_code(q), workspace.data_ptr(), nbytes,
                                   _stream_handle(q, stream))
+    _check(st)
+
+
+def mattn_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, workspace, stages: int,
+                     causal: bool = False, scale: Optional[float] = None, stream=None) -> None:
+    """Enqueue only the selected backward stages (MATTN_BWD_* flags), in the
+    order preprocess, dK/dV, dQ; all three together are exactly mattn_bwd."""
+    _require(q, k, v, o, lse, do, dq, dk, dv, workspace)
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    nbytes = workspace.numel() * workspace.element_size()
+    st = load_library().mattn_bwd_stages(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                                         dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
+                                         int(causal), float(scale), _dtype_code(q),
+                                         workspace.data_ptr(), nbytes, int(stages),
+                                         _stream_handle(q, stream))
     _check(st)
 
 

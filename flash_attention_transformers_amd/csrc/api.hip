@@ -83,11 +83,13 @@ size_t mattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D) 
   return dlt_bytes(B, Hq, Sq) + part_bytes(B, Hkv, Sq, Skv, D);
 }
 
-mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* o,
-                       const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
-                       int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
-                       mattn_dtype dtype, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+mattn_status mattn_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                              float scale, mattn_dtype dtype, void* workspace,
+                              size_t workspace_bytes, unsigned stages, hipStream_t stream) {
+  const unsigned all = MATTN_BWD_PREPROCESS | MATTN_BWD_DKDV | MATTN_BWD_DQ;
+  if (stages == 0 || (stages & ~all) != 0) return MATTN_ERR_INVALID_ARG;
   Sizes sz;
   mattn_status st = check_args(B, Hq, Hkv, Sq, Skv, D, causal, scale, dtype, &sz);
   if (st != MATTN_OK) return st;
@@ -99,6 +101,7 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
   }
   if (sz.rows == 0) {
     // No query rows: every key receives a zero gradient.
+    if (!(stages & MATTN_BWD_DKDV)) return MATTN_OK;
     const size_t words = (size_t)sz.kv_elems * (dtype == MATTN_BF16 ? 2 : 4) / 4;
     if (mattn::launch_zero_words(dk, words, stream) != hipSuccess) return MATTN_ERR_LAUNCH;
     if (mattn::launch_zero_words(dv, words, stream) != hipSuccess) return MATTN_ERR_LAUNCH;
@@ -107,14 +110,36 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
   const mattn::Problem p{B, Hq, Hkv, Sq, Skv, D, causal, scale};
   float* dlt = (float*)workspace;
   float* part = (float*)((char*)workspace + dlt_bytes(B, Hq, Sq));
-  hipError_t e = mattn::launch_bwd_preprocess(p, dtype == MATTN_BF16, o, dout, dlt, stream);
-  if (e != hipSuccess) return MATTN_ERR_LAUNCH;
-  if (dtype == MATTN_BF16)
-    e = mattn::launch_bwd_bf16(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream);
-  else
-    e = mattn::launch_bwd_f32(p, (const float*)q, (const float*)k, (const float*)v, lse, dlt,
-                              (const float*)dout, (float*)dq, (float*)dk, (float*)dv, stream);
-  return e == hipSuccess ? MATTN_OK : MATTN_ERR_LAUNCH;
+  const bool bf = dtype == MATTN_BF16;
+  if (stages & MATTN_BWD_PREPROCESS) {
+    if (mattn::launch_bwd_preprocess(p, bf, o, dout, dlt, stream) != hipSuccess)
+      return MATTN_ERR_LAUNCH;
+  }
+  if (stages & MATTN_BWD_DKDV) {
+    const hipError_t e =
+        bf ? mattn::launch_dkdv_bf16(p, q, k, v, lse, dlt, dout, dk, dv, part, stream)
+           : mattn::launch_dkdv_f32(p, (const float*)q, (const float*)k, (const float*)v, lse,
+                                    dlt, (const float*)dout, (float*)dk, (float*)dv, stream);
+    if (e != hipSuccess) return MATTN_ERR_LAUNCH;
+  }
+  if (stages & MATTN_BWD_DQ) {
+    const hipError_t e =
+        bf ? mattn::launch_dq_bf16(p, q, k, v, lse, dlt, dout, dq, stream)
+           : mattn::launch_dq_f32(p, (const float*)q, (const float*)k, (const float*)v, lse, dlt,
+                                  (const float*)dout, (float*)dq, stream);
+    if (e != hipSuccess) return MATTN_ERR_LAUNCH;
+  }
+  return MATTN_OK;
+}
+
+mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                       int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                       mattn_dtype dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  return mattn_bwd_stages(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, causal,
+                          scale, dtype, workspace, workspace_bytes,
+                          MATTN_BWD_PREPROCESS | MATTN_BWD_DKDV | MATTN_BWD_DQ, stream);
 }
 
 const char* mattn_strerror(mattn_status s) {

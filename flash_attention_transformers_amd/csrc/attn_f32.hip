@@ -230,21 +230,24 @@ hipError_t fwd_f32_t(const Problem& p, const float* q, const float* k, const flo
 }
 
 template <int D, bool CAUSAL>
-hipError_t bwd_f32_t(const Problem& p, const float* q, const float* k, const float* v,
-                     const float* lse, const float* dlt, const float* dout, float* dq, float* dk,
-                     float* dv, hipStream_t stream) {
-  const int G = p.Hq / p.Hkv;
-  const float c = p.scale * MATTN_LOG2E;
+hipError_t dkdv_f32_t(const Problem& p, const float* q, const float* k, const float* v,
+                      const float* lse, const float* dlt, const float* dout, float* dk, float* dv,
+                      hipStream_t stream) {
   const int n_kt = (p.Skv + F_ROWS - 1) / F_ROWS;
   hipLaunchKernelGGL((dkdv_f32_kernel<D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hkv * n_kt)),
-                     dim3(F_THREADS), 0, stream, q, k, v, dout, lse, dlt, dk, dv, p.Hq, G, p.Sq,
-                     p.Skv, p.scale, c, n_kt);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+                     dim3(F_THREADS), 0, stream, q, k, v, dout, lse, dlt, dk, dv, p.Hq,
+                     p.Hq / p.Hkv, p.Sq, p.Skv, p.scale, p.scale * MATTN_LOG2E, n_kt);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t dq_f32_t(const Problem& p, const float* q, const float* k, const float* v,
+                    const float* lse, const float* dlt, const float* dout, float* dq,
+                    hipStream_t stream) {
   const int n_rt = (p.Sq + F_ROWS - 1) / F_ROWS;
   hipLaunchKernelGGL((dq_f32_kernel<D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * n_rt)),
-                     dim3(F_THREADS), 0, stream, q, k, v, dout, lse, dlt, dq, p.Hq, G, p.Sq, p.Skv,
-                     p.scale, c, n_rt);
+                     dim3(F_THREADS), 0, stream, q, k, v, dout, lse, dlt, dq, p.Hq, p.Hq / p.Hkv,
+                     p.Sq, p.Skv, p.scale, p.scale * MATTN_LOG2E, n_rt);
   return hipGetLastError();
 }
 
@@ -258,14 +261,24 @@ hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, cons
                   : fwd_f32_t<128, false>(p, q, k, v, o, lse, stream);
 }
 
-hipError_t launch_bwd_f32(const Problem& p, const float* q, const float* k, const float* v,
-                          const float* lse, const float* dlt, const float* dout, float* dq,
-                          float* dk, float* dv, hipStream_t stream) {
+hipError_t launch_dkdv_f32(const Problem& p, const float* q, const float* k, const float* v,
+                           const float* lse, const float* dlt, const float* dout, float* dk,
+                           float* dv, hipStream_t stream) {
   if (p.D == 64)
-    return p.causal ? bwd_f32_t<64, true>(p, q, k, v, lse, dlt, dout, dq, dk, dv, stream)
-                    : bwd_f32_t<64, false>(p, q, k, v, lse, dlt, dout, dq, dk, dv, stream);
-  return p.causal ? bwd_f32_t<128, true>(p, q, k, v, lse, dlt, dout, dq, dk, dv, stream)
-                  : bwd_f32_t<128, false>(p, q, k, v, lse, dlt, dout, dq, dk, dv, stream);
+    return p.causal ? dkdv_f32_t<64, true>(p, q, k, v, lse, dlt, dout, dk, dv, stream)
+                    : dkdv_f32_t<64, false>(p, q, k, v, lse, dlt, dout, dk, dv, stream);
+  return p.causal ? dkdv_f32_t<128, true>(p, q, k, v, lse, dlt, dout, dk, dv, stream)
+                  : dkdv_f32_t<128, false>(p, q, k, v, lse, dlt, dout, dk, dv, stream);
+}
+
+hipError_t launch_dq_f32(const Problem& p, const float* q, const float* k, const float* v,
+                         const float* lse, const float* dlt, const float* dout, float* dq,
+                         hipStream_t stream) {
+  if (p.D == 64)
+    return p.causal ? dq_f32_t<64, true>(p, q, k, v, lse, dlt, dout, dq, stream)
+                    : dq_f32_t<64, false>(p, q, k, v, lse, dlt, dout, dq, stream);
+  return p.causal ? dq_f32_t<128, true>(p, q, k, v, lse, dlt, dout, dq, stream)
+                  : dq_f32_t<128, false>(p, q, k, v, lse, dlt, dout, dq, stream);
 }
 
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t stream) {

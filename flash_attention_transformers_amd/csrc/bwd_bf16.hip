@@ -183,17 +183,30 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     __syncthreads();
     if (it + 1 < n_it) load_it(it + 1);
 
-    const bool masked = CAUSAL && (kw0 + 31 > qt0 + diag);
     float* pex = Pex + slice * (NSUB * 4 * 64 * 4);
-    if (pwave) {
-      // S = Q K^T (lane = key column, regs = query rows) -> P.
+    auto pwave_step = [&](auto masked) {
+      constexpr bool MASK = decltype(masked)::value;
+      // S = Q K^T (lane = key column, regs = query rows), both sub-blocks
+      // as independent MFMA chains over one batch of operand reads.
+      f32x16 sa[NSUB];
+#pragma unroll
+      for (int qb = 0; qb < NSUB; ++qb) sa[qb] = zero_f32x16();
+#pragma unroll
+      for (int st0 = 0; st0 < D / 16; st0 += 4) {
+        bf16x8 a[NSUB][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int qb = 0; qb < NSUB; ++qb)
+            a[qb][u] = ld_row_operand(Qs, P, qb * 32, 16 * (st0 + u), lane);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int qb = 0; qb < NSUB; ++qb) sa[qb] = mfma32(a[qb][u], kvf[st0 + u], sa[qb]);
+      }
       bf16x8 pb[NSUB][2];
 #pragma unroll
-      for (int qb = 0; qb < NSUB; ++qb) {
-        f32x16 sa = zero_f32x16();
-#pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-          sa = mfma32(ld_row_operand(Qs, P, qb * 32, 16 * st, lane), kvf[st], sa);
+      for (int qb = 0; qb < NSUB; ++qb)
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
           const f32x4 L = *reinterpret_cast<const f32x4*>(&lse_s[qb * 32 + 8 * blk + 4 * g]);
@@ -201,33 +214,49 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i = 4 * blk + j;
-            float pr = fast_exp2(__builtin_fmaf(sa[i], c, -L[j]));
-            if (masked && key > qt0 + qb * 32 + crow(i, g) + diag) pr = 0.f;
+            float pr = fast_exp2(__builtin_fmaf(sa[qb][i], c, -L[j]));
+            if (MASK && key > qt0 + qb * 32 + crow(i, g) + diag) pr = 0.f;
             pv[j] = pr;
             pb[qb][i >> 3][i & 7] = (bf16)pr;
           }
           *reinterpret_cast<f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]) = pv;
         }
-      }
       __syncthreads();
       // dV^T += dO^T P.
 #pragma unroll
       for (int qb = 0; qb < NSUB; ++qb)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+          bf16x8 a[D / 32];
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
-            acc[db] = mfma32(ld_trans_operand(dOs, P, qb * 32 + 16 * t, db * 32, lane),
-                             pb[qb][t], acc[db]);
+            a[db] = ld_trans_operand(dOs, P, qb * 32 + 16 * t, db * 32, lane);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[qb][t], acc[db]);
+        }
+    };
+    if (pwave) {
+      if (CAUSAL && (kw0 + 31 > qt0 + diag))
+        pwave_step(std::true_type{});
+      else
+        pwave_step(std::false_type{});
     } else {
       // dP = dO V^T, same layout as S.
       f32x16 dp[NSUB];
 #pragma unroll
-      for (int qb = 0; qb < NSUB; ++qb) {
-        dp[qb] = zero_f32x16();
+      for (int qb = 0; qb < NSUB; ++qb) dp[qb] = zero_f32x16();
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st)
-          dp[qb] = mfma32(ld_row_operand(dOs, P, qb * 32, 16 * st, lane), kvf[st], dp[qb]);
+      for (int st0 = 0; st0 < D / 16; st0 += 4) {
+        bf16x8 a[NSUB][4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int qb = 0; qb < NSUB; ++qb)
+            a[qb][u] = ld_row_operand(dOs, P, qb * 32, 16 * (st0 + u), lane);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int qb = 0; qb < NSUB; ++qb) dp[qb] = mfma32(a[qb][u], kvf[st0 + u], dp[qb]);
       }
       __syncthreads();
       // dS = P (dP - Dlt); dK^T += Q^T dS.
@@ -245,11 +274,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           }
         }
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t) {
+          bf16x8 a[D / 32];
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
-            acc[db] = mfma32(ld_trans_operand(Qs, P, qb * 32 + 16 * t, db * 32, lane),
-                             dsb[t], acc[db]);
+            a[db] = ld_trans_operand(Qs, P, qb * 32 + 16 * t, db * 32, lane);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], dsb[t], acc[db]);
+        }
       }
     }
   }
@@ -458,35 +490,38 @@ hipError_t launch_pre_t(const Problem& p, const void* o, const void* dout, float
 }
 
 template <int D, bool CAUSAL>
-hipError_t launch_bwd_t(const Problem& p, const void* q, const void* k, const void* v,
-                        const float* lse, const float* dlt, const void* dout, void* dq, void* dk,
-                        void* dv, float* part, hipStream_t stream) {
+hipError_t launch_dkdv_t(const Problem& p, const void* q, const void* k, const void* v,
+                         const float* lse, const float* dlt, const void* dout, void* dk, void* dv,
+                         float* part, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const float c = p.scale * MATTN_LOG2E;
   const int n_kt = (p.Skv + BWD_BN - 1) / BWD_BN;
   const int nsplit = bwd_nsplit(p.B, p.Hkv, p.Sq, p.Skv);
-  const int n_qt32 = (p.Sq + BWD_BMQ - 1) / BWD_BMQ;
-  const int q_chunk = ((n_qt32 + nsplit - 1) / nsplit) * BWD_BMQ;
+  const int n_qt = (p.Sq + BWD_BMQ - 1) / BWD_BMQ;
+  const int q_chunk = ((n_qt + nsplit - 1) / nsplit) * BWD_BMQ;
   const long long blocks = (long long)p.B * p.Hkv * n_kt * nsplit;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(DKDV_THREADS), 0,
                      stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (const bf16*)dout,
                      lse, dlt, (bf16*)dk, (bf16*)dv, part, p.Hq, G, p.Sq, p.Skv, p.scale, c,
                      n_kt, nsplit, q_chunk);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (nsplit > 1) {
-    const long long total4 = (long long)p.B * p.Hkv * p.Skv * D / 4;
-    hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((total4 + THREADS - 1) / THREADS)),
-                       dim3(THREADS), 0, stream, (const float*)part, (bf16*)dk, (bf16*)dv, nsplit,
-                       p.B * p.Hkv, p.Skv, n_kt, D, p.scale);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  if (e != hipSuccess || nsplit == 1) return e;
+  const long long total4 = (long long)p.B * p.Hkv * p.Skv * D / 4;
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((total4 + THREADS - 1) / THREADS)),
+                     dim3(THREADS), 0, stream, (const float*)part, (bf16*)dk, (bf16*)dv, nsplit,
+                     p.B * p.Hkv, p.Skv, n_kt, D, p.scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const Problem& p, const void* q, const void* k, const void* v,
+                       const float* lse, const float* dlt, const void* dout, void* dq,
+                       hipStream_t stream) {
   const int n_qt = (p.Sq + DQ_BM - 1) / DQ_BM;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * n_qt)),
                      dim3(THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                     (const bf16*)dout, lse, dlt, (bf16*)dq, p.Hq, G, p.Sq, p.Skv, p.scale, c,
-                     n_qt);
+                     (const bf16*)dout, lse, dlt, (bf16*)dq, p.Hq, p.Hq / p.Hkv, p.Sq, p.Skv,
+                     p.scale, p.scale * MATTN_LOG2E, n_qt);
   return hipGetLastError();
 }
 
@@ -498,14 +533,24 @@ hipError_t launch_bwd_preprocess(const Problem& p, bool bf16_io, const void* o, 
                  : launch_pre_t<float>(p, o, dout, dlt, stream);
 }
 
-hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v,
-                           const float* lse, const float* dlt, const void* dout, void* dq,
-                           void* dk, void* dv, float* part, hipStream_t stream) {
+hipError_t launch_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                            const float* lse, const float* dlt, const void* dout, void* dk,
+                            void* dv, float* part, hipStream_t stream) {
   if (p.D == 64)
-    return p.causal ? launch_bwd_t<64, true>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream)
-                    : launch_bwd_t<64, false>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream);
-  return p.causal ? launch_bwd_t<128, true>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream)
-                  : launch_bwd_t<128, false>(p, q, k, v, lse, dlt, dout, dq, dk, dv, part, stream);
+    return p.causal ? launch_dkdv_t<64, true>(p, q, k, v, lse, dlt, dout, dk, dv, part, stream)
+                    : launch_dkdv_t<64, false>(p, q, k, v, lse, dlt, dout, dk, dv, part, stream);
+  return p.causal ? launch_dkdv_t<128, true>(p, q, k, v, lse, dlt, dout, dk, dv, part, stream)
+                  : launch_dkdv_t<128, false>(p, q, k, v, lse, dlt, dout, dk, dv, part, stream);
+}
+
+hipError_t launch_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                          const float* lse, const float* dlt, const void* dout, void* dq,
+                          hipStream_t stream) {
+  if (p.D == 64)
+    return p.causal ? launch_dq_t<64, true>(p, q, k, v, lse, dlt, dout, dq, stream)
+                    : launch_dq_t<64, false>(p, q, k, v, lse, dlt, dout, dq, stream);
+  return p.causal ? launch_dq_t<128, true>(p, q, k, v, lse, dlt, dout, dq, stream)
+                  : launch_dq_t<128, false>(p, q, k, v, lse, dlt, dout, dq, stream);
 }
 
 }  // namespace mattn

@@ -24,17 +24,23 @@ hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const
 hipError_t launch_bwd_preprocess(const Problem& p, bool bf16_io, const void* o,
                                  const void* dout, float* dlt, hipStream_t stream);
 
-// dK/dV (+ split reduction) and dQ for bf16; `part` is fp32 scratch of
+// dK/dV (+ split reduction) for bf16; `part` is fp32 scratch of
 // 2 * nsplit * B*Hkv*ceil(Skv/BWD_BN)*BWD_BN*D floats when nsplit > 1.
-hipError_t launch_bwd_bf16(const Problem& p, const void* q, const void* k, const void* v,
-                           const float* lse, const float* dlt, const void* dout, void* dq,
-                           void* dk, void* dv, float* part, hipStream_t stream);
+hipError_t launch_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                            const float* lse, const float* dlt, const void* dout, void* dk,
+                            void* dv, float* part, hipStream_t stream);
+hipError_t launch_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
+                          const float* lse, const float* dlt, const void* dout, void* dq,
+                          hipStream_t stream);
 
 hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v,
                           float* o, float* lse, hipStream_t stream);
-hipError_t launch_bwd_f32(const Problem& p, const float* q, const float* k, const float* v,
-                          const float* lse, const float* dlt, const float* dout, float* dq,
-                          float* dk, float* dv, hipStream_t stream);
+hipError_t launch_dkdv_f32(const Problem& p, const float* q, const float* k, const float* v,
+                           const float* lse, const float* dlt, const float* dout, float* dk,
+                           float* dv, hipStream_t stream);
+hipError_t launch_dq_f32(const Problem& p, const float* q, const float* k, const float* v,
+                         const float* lse, const float* dlt, const float* dout, float* dq,
+                         hipStream_t stream);
 
 // Zero-fill of n 4-byte words (used for dk/dv when there are no query rows).
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t stream);

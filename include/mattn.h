@@ -96,6 +96,22 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
                        float scale, mattn_dtype dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
 
+/* The stages mattn_bwd enqueues, selectable for callers that schedule or
+ * time them separately.  Same arguments, checks and workspace as mattn_bwd;
+ * `stages` is a non-zero OR of the flags below.  Stages must run in this
+ * order (each reads what the one before wrote into `workspace` or the
+ * outputs); calling mattn_bwd_stages with all three flags is exactly
+ * mattn_bwd.  A stage not selected leaves its outputs untouched.
+ *   MATTN_BWD_PREPROCESS  D = sum(dO * O) per query row into the workspace
+ *   MATTN_BWD_DKDV        dK, dV (needs the preprocess result)
+ *   MATTN_BWD_DQ          dQ     (needs the preprocess result) */
+enum { MATTN_BWD_PREPROCESS = 1, MATTN_BWD_DKDV = 2, MATTN_BWD_DQ = 4 };
+mattn_status mattn_bwd_stages(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                              int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                              float scale, mattn_dtype dtype, void* workspace,
+                              size_t workspace_bytes, unsigned stages, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* mattn_strerror(mattn_status s);
 

@@ -26,7 +26,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["mattn_fwd", "mattn_bwd", "mattn_bwd_workspace_size", "mattn_strerror", "mattn_version"])
+        ["mattn_fwd", "mattn_bwd", "mattn_bwd_stages", "mattn_bwd_workspace_size", "mattn_strerror",
+         "mattn_version"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -114,3 +115,21 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         fa.fwd(q, q, q)
+
+
+@pytest.mark.parametrize("stages", [0, 8, 0xFF])
+def test_bwd_stages_rejects_bad_mask(stages):
+    lib = fa.load_library()
+    st = lib.mattn_bwd_stages(P, P, P, P, P, P, P, P, P, 1, 2, 2, 128, 128, 64, 0, 0.125, 0, P,
+                              1 << 40, stages, None)
+    assert st == fa.MATTN_ERR_INVALID_ARG
+
+
+def test_bwd_stages_validates_like_bwd():
+    lib = fa.load_library()
+    st = lib.mattn_bwd_stages(P, P, P, P, P, P, P, P, P, 1, 3, 2, 128, 128, 64, 0, 0.125, 0, P,
+                              1 << 40, fa.MATTN_BWD_ALL, None)
+    assert st == fa.MATTN_ERR_INVALID_ARG
+    st = lib.mattn_bwd_stages(P, P, P, P, P, P, P, P, P, 1, 2, 2, 128, 128, 96, 0, 0.125, 0, P,
+                              1 << 40, fa.MATTN_BWD_DKDV, None)
+    assert st == fa.MATTN_ERR_UNSUPPORTED

@@ -199,3 +199,27 @@ def test_negative_and_zero_scale(dev):
                 assert H.rel_l2(H.to_np(g["dk"]), rdk) <= tol["grad_rel_l2"]
             else:
                 assert np.abs(H.to_np(g["dq"])).max() == 0 and np.abs(H.to_np(g["dk"])).max() == 0
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 300, 300, 128, True), (1, 2, 2, 1000, 257, 128, False),
+                                   (1, 2, 2, 100, 70, 64, False)])
+def test_stage_sequence_equals_bwd(shape, dev):
+    """Preprocess, dK/dV and dQ enqueued separately give mattn_bwd's bits."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D, causal = shape
+    H.say(f"[stages] {shape}")
+    w = W.Workload("stages", B, Hq, Hkv, Sq, Skv, D, causal, "bf16", 23, True)
+    t = W.to_torch(W.make_inputs(w), dev)
+    ref = fwd_bwd(t, causal)
+    dq, dk, dv = (torch.full_like(ref[n], float("nan")) for n in ("dq", "dk", "dv"))
+    ws = fa.bwd_workspace(t["q"], t["k"])
+    args = (t["q"], t["k"], t["v"], ref["o"], ref["lse"], t["do"], dq, dk, dv, ws)
+    fa.mattn_bwd_stages(*args, fa.MATTN_BWD_PREPROCESS, causal)
+    fa.mattn_bwd_stages(*args, fa.MATTN_BWD_DQ, causal)
+    torch.cuda.synchronize()
+    assert torch.isnan(dk.float()).all() and torch.isnan(dv.float()).all()  # not selected yet
+    fa.mattn_bwd_stages(*args, fa.MATTN_BWD_DKDV, causal)
+    torch.cuda.synchronize()
+    for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.equal(x.view(torch.int16), ref[n].view(torch.int16)), n
