@@ -106,8 +106,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bool pwave = wave < 4;
   const int Hkv = Hq / G;
 
-  const int split = blockIdx.x % nsplit;
-  const int rest = blockIdx.x / nsplit;
+  // XCD-aware order: consecutive workgroup ids go round-robin to the 8 XCDs,
+  // so remap them so each XCD walks a contiguous run of (KV head, key tile,
+  // chunk) ids; the key tiles of one KV head then read the same Q/dO tiles
+  // through one L2.
+  const int nblk = gridDim.x;
+  const int L = ((nblk & 7) == 0) ? (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  const int split = L % nsplit;
+  const int rest = L / nsplit;
   const int kt = rest % n_kt;
   const int bkv = rest / n_kt;
   const int b = bkv / Hkv, kvh = bkv % Hkv;
@@ -351,30 +357,39 @@ void bwd_reduce_kernel(const float* __restrict__ part, bf16* __restrict__ dK,
 constexpr int DQ_BM = 128;
 constexpr int DQ_BN = 64;
 
+constexpr int DQ_THREADS = 512;  // 4 query slices x 2 key halves
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(THREADS, (D == 128 ? 1 : 2))
+__global__ __launch_bounds__(DQ_THREADS)
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ DLT,
                    bf16* __restrict__ dQ, int Hq, int G, int Sq, int Skv, float scale, float c,
                    int n_qt) {
   constexpr int P = TilePitch<D>::value;
-  constexpr int CH = DQ_BN * D / 8 / THREADS;  // 16-byte chunks per thread per tensor
-  __shared__ __attribute__((aligned(16))) bf16 Ks[DQ_BN * P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[DQ_BN * P];
+  constexpr int CH = DQ_BN * D / 8 / DQ_THREADS;  // 16-byte chunks per thread per tensor
+  static_assert(CH >= 1 && (DQ_BN * D / 8) % DQ_THREADS == 0, "tile loader must tile the workgroup");
+  // K and V tiles during the walk; afterwards the same LDS holds the
+  // key-half partials of dQ^T: [slice][db][r][lane][4] floats.
+  constexpr int TILE_BYTES = 2 * DQ_BN * P * 2;
+  constexpr int RED_BYTES = 4 * (D / 32) * 4 * 64 * 4 * 4;
+  __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES];
+  bf16* Ks = reinterpret_cast<bf16*>(smem);
+  bf16* Vs = Ks + DQ_BN * P;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
+  const int slice = wave & 3;   // 32 query rows
+  const int kh = wave >> 2;     // which 32-key half of every tile this wave takes
   int bh, qt;
   tile_of_block(blockIdx.x, gridDim.x / n_qt, n_qt, CAUSAL, bh, qt);
   const int h = bh % Hq, b = bh / Hq;
   const int Hkv = Hq / G;
   const size_t kv_off = ((size_t)(b * Hkv + h / G) * Skv) * D;
   const int q0 = qt * DQ_BM;
-  const int qw0 = q0 + wave * 32;
+  const int qw0 = q0 + slice * 32;
   const int qrow = qw0 + l32;
   const int diag = Skv - Sq;
-  const size_t qo = ((size_t)bh * Sq + qrow) * D;
 
   const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
   const Buf dobuf(dO + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
@@ -398,14 +413,14 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   auto load_tile = [&](int j0) {
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
-      const int ch = tid + THREADS * r;
+      const int ch = tid + DQ_THREADS * r;
       const uint32_t off = (uint32_t)((j0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2;
       kreg[r] = kbuf.ld16(off);
       vreg[r] = vbuf.ld16(off);
     }
   };
 
-  f32x16 adq[D / 32];
+  f32x16 adq[D / 32];  // partial dQ^T over this wave's key halves
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adq[db] = zero_f32x16();
 
@@ -415,7 +430,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
-      const int ch = tid + THREADS * r;
+      const int ch = tid + DQ_THREADS * r;
       const int o = (ch / (D / 8)) * P + (ch % (D / 8)) * 8;
       *reinterpret_cast<uint4*>(&Ks[o]) = kreg[r];
       *reinterpret_cast<uint4*>(&Vs[o]) = vreg[r];
@@ -423,51 +438,76 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     __syncthreads();
     if (kt + 1 < n_kt) load_tile(j0 + DQ_BN);
 
+    const int kb0 = kh * 32;  // this wave's 32 keys of the tile
     auto step = [&](auto masked) {
       constexpr bool MASK = decltype(masked)::value;
+      f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 s = zero_f32x16(), dp = zero_f32x16();
+      for (int st0 = 0; st0 < D / 16; st0 += 4) {
+        bf16x8 ak[4], av[4];
 #pragma unroll
-        for (int st = 0; st < D / 16; ++st) {
-          s = mfma32(ld_row_operand(Ks, P, kb * 32, 16 * st, lane), qf[st], s);
-          dp = mfma32(ld_row_operand(Vs, P, kb * 32, 16 * st, lane), dof[st], dp);
+        for (int u = 0; u < 4; ++u) {
+          ak[u] = ld_row_operand(Ks, P, kb0, 16 * (st0 + u), lane);
+          av[u] = ld_row_operand(Vs, P, kb0, 16 * (st0 + u), lane);
         }
-        bf16x8 dsb[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
-          if (MASK) {
-            const int kk = j0 + kb * 32 + crow(i, g);
-            if (kk >= Skv || (CAUSAL && kk > qrow + diag)) p = 0.f;
-          }
-          dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dl));
+        for (int u = 0; u < 4; ++u) {
+          s = mfma32(ak[u], qf[st0 + u], s);
+          dp = mfma32(av[u], dof[st0 + u], dp);
         }
-        // dQ^T += K^T dS^T
+      }
+      bf16x8 dsb[2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int i = 0; i < 16; ++i) {
+        float p = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
+        if (MASK) {
+          const int kk = j0 + kb0 + crow(i, g);
+          if (kk >= Skv || (CAUSAL && kk > qrow + diag)) p = 0.f;
+        }
+        dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dl));
+      }
+      // dQ^T += K^T dS^T over this wave's 32 keys.
 #pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            adq[db] = mfma32(ld_trans_operand(Ks, P, kb * 32 + 16 * t, db * 32, lane), dsb[t],
-                             adq[db]);
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 a[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          a[db] = ld_trans_operand(Ks, P, kb0 + 16 * t, db * 32, lane);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) adq[db] = mfma32(a[db], dsb[t], adq[db]);
       }
     };
-    if ((j0 + DQ_BN > Skv) || (CAUSAL && (j0 + DQ_BN - 1 > qw0 + diag)))
+    const bool masked = (j0 + kb0 + 32 > Skv) || (CAUSAL && (j0 + kb0 + 31 > qw0 + diag));
+    if (masked)
       step(std::true_type{});
     else
       step(std::false_type{});
   }
 
-  if (qrow < Sq) {
-    bf16* prow = dQ + qo;
+  // Sum the two key-half partials in a fixed order (half 0 + half 1) through
+  // LDS, reusing the K tile buffer, and write dQ.
+  __syncthreads();
+  float* red_slice = reinterpret_cast<float*>(smem) + slice * (D / 32) * 16 * 64;
+  if (kh == 1) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; i += 4)
+        *reinterpret_cast<f32x4*>(&red_slice[((db * 4 + i / 4) * 64 + lane) * 4]) =
+            f32x4{adq[db][i], adq[db][i + 1], adq[db][i + 2], adq[db][i + 3]};
+  }
+  __syncthreads();
+  if (kh == 0 && qrow < Sq) {
+    bf16* prow = dQ + ((size_t)bh * Sq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(&red_slice[((db * 4 + r) * 64 + lane) * 4]);
         const int d = db * 32 + r * 8 + g * 4;
         uint2 w;
-        w.x = pack_bf16x2(adq[db][4 * r] * scale, adq[db][4 * r + 1] * scale);
-        w.y = pack_bf16x2(adq[db][4 * r + 2] * scale, adq[db][4 * r + 3] * scale);
+        w.x = pack_bf16x2((adq[db][4 * r] + o[0]) * scale, (adq[db][4 * r + 1] + o[1]) * scale);
+        w.y = pack_bf16x2((adq[db][4 * r + 2] + o[2]) * scale, (adq[db][4 * r + 3] + o[3]) * scale);
         *reinterpret_cast<uint2*>(prow + d) = w;
       }
   }
@@ -519,7 +559,7 @@ hipError_t launch_dq_t(const Problem& p, const void* q, const void* k, const voi
                        hipStream_t stream) {
   const int n_qt = (p.Sq + DQ_BM - 1) / DQ_BM;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * n_qt)),
-                     dim3(THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                     dim3(DQ_THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
                      (const bf16*)dout, lse, dlt, (bf16*)dq, p.Hq, p.Hq / p.Hkv, p.Sq, p.Skv,
                      p.scale, p.scale * MATTN_LOG2E, n_qt);
   return hipGetLastError();
