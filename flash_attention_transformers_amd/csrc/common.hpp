@@ -41,14 +41,41 @@ __device__ __forceinline__ constexpr int crow(int i, int g) {
   return (i >> 2) * 8 + g * 4 + (i & 3);
 }
 
-// A operand of mfma32 holding the TRANSPOSE of a row-major bf16 tile in LDS:
+// LDS tile pitches (bf16 elements).  A [rows x D] tile is stored row-major
+// with a padded pitch chosen for the way it is read (64 four-byte banks, 256
+// bytes):
+//   * row operands: 16 lanes read 16 bytes from 16 consecutive rows; pitch
+//     304 B (D = 128) / 208 B (D = 64) puts them in 16 distinct bank quads;
+//   * transposed operands: 32 lanes read 64 bytes from each of 4 consecutive
+//     rows; pitch 320 B (D = 128) / 192 B (D = 64) puts the 4 rows in
+//     disjoint 64-byte bank segments.
+// No single pitch serves both, so a tile read both ways is stored twice.
+// Measured on MI355X: 197 (rows, 304 B) and 182 (transposed, 320 B) bytes per
+// clock per CU, against 62 and 116 with the pitches swapped.
+template <int D>
+struct RowPitch {
+  static constexpr int value = D == 128 ? 152 : 104;
+};
+template <int D>
+struct TrPitch {
+  static constexpr int value = D == 128 ? 160 : 96;
+};
+
+// A operand of mfma32 read straight from a row-major tile in LDS: lane row
+// l32 = tile row row0 + l32, k-slots 8g..8g+7 = columns col0 + 8g ...
+__device__ __forceinline__ bf16x8 ld_row_operand(const bf16* tile, int pitch, int row0, int col0,
+                                                 int lane) {
+  return *reinterpret_cast<const bf16x8*>(&tile[(row0 + (lane & 31)) * pitch + col0 + 8 * (lane >> 5)]);
+}
+
+// A operand of mfma32 holding the TRANSPOSE of a row-major tile in LDS:
 // operand row r (lane row l32) is tile column col0 + r, and k-slot 8g + e of
 // the k-step is tile row row0 + swz(8g + e), the order in which a C tile fed
 // as the B operand carries its rows.  Built from two ds_read_b64_tr_b16: in
 // each 16-lane group that instruction hands lane i element (i % 4) of the
-// 8-byte chunk read by source lane 4e + i/4, so source lane s of group j reads
-// tile row row0 + 8h + 4(j/2) + s/4 at columns col0 + 16(j%2) + 4(s%4) .. +3.
-// `pitch` (elements) must be a multiple of 4.
+// 8-byte chunk read by source lane 4e + i/4, so source lane s of group j
+// reads tile row row0 + 8h + 4(j/2) + s/4 at columns col0 + 16(j%2) + 4(s%4)
+// .. +3.  `pitch` must be a multiple of 4.
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8 ld_trans_operand(const bf16* tile, int pitch, int row0,
                                                    int col0, int lane) {
@@ -59,22 +86,6 @@ __device__ __forceinline__ bf16x8 ld_trans_operand(const bf16* tile, int pitch, 
   const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * pitch));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-
-// A operand of mfma32 read straight from a row-major bf16 tile in LDS:
-// lane row l32 = tile row row0 + l32, k-slots 8g..8g+7 = columns col0 + 8g ...
-__device__ __forceinline__ bf16x8 ld_row_operand(const bf16* tile, int pitch, int row0, int col0,
-                                                 int lane) {
-  return *reinterpret_cast<const bf16x8*>(&tile[(row0 + (lane & 31)) * pitch + col0 + 8 * (lane >> 5)]);
-}
-
-// LDS row pitch (bf16 elements) for [rows x D] tiles read both by rows (16 B
-// per lane, 16 consecutive rows) and by ld_trans_operand (4 consecutive rows,
-// 32 B each): with 64 four-byte banks both patterns hit distinct banks when
-// the pitch is 304 B (D = 128) or 208 B (D = 64).
-template <int D>
-struct TilePitch {
-  static constexpr int value = D == 128 ? 152 : 104;
-};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -113,6 +124,51 @@ struct Buf {
   }
   __device__ __forceinline__ float ldf(uint32_t off) const {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+  }
+};
+
+// Direct global -> LDS copy of 16 bytes per lane: lane L's bytes land at
+// lds_base + 16 L (lds_base wave-uniform).  Offsets outside the descriptor's
+// range write zeros.  Completion is tracked by vmcnt, like other vector
+// memory loads.
+__device__ __forceinline__ void ld16_to_lds(const Buf& b, uint32_t off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                           off, 0, 0, 0);
+}
+
+// A tile of `ROWS` rows x D bf16 with row pitch PITCH (elements), filled by
+// ld16_to_lds.  The tile's LDS bytes are split into 16-byte slots, slot q =
+// row * (PITCH / 8) + chunk; the workgroup's NT threads cover the slots in
+// rounds of NT, so each wave writes one contiguous kilobyte per round.  A
+// slot in a row's padding gets an out-of-range offset and is written as
+// zeros.  The per-thread global offsets depend only on the thread, so they
+// are computed once; per tile only the descriptor base moves.
+template <int D, int ROWS, int PITCH, int NT>
+struct DirectTile {
+  static constexpr int SLOTS_PER_ROW = PITCH / 8;
+  static constexpr int SLOTS = ROWS * SLOTS_PER_ROW;
+  static constexpr int ROUNDS = (SLOTS + NT - 1) / NT;
+  static_assert(PITCH % 8 == 0 && PITCH >= D, "pitch");
+  uint32_t off[ROUNDS];
+  __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int q = r * NT + tid;
+      const int row = q / SLOTS_PER_ROW, c = q - row * SLOTS_PER_ROW;
+      off[r] = (c < D / 8) ? (uint32_t)(row * D + c * 8) * 2 : 0x80000000u;
+    }
+  }
+  // Copy rows [0, ROWS) of `src` (a descriptor whose base is the tile's first
+  // row) into `lds` (the tile, PITCH-padded).  Slots past the tile's end are
+  // skipped (a whole wave at a time, since SLOTS is a multiple of 64).
+  __device__ __forceinline__ void load(const Buf& src, bf16* lds, int tid) const {
+    static_assert(SLOTS % 64 == 0, "partial rounds must end on a wave boundary");
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int q0 = r * NT + (tid & ~63);  // first slot of this wave in round r
+      if (SLOTS % NT == 0 || q0 < SLOTS)
+        ld16_to_lds(src, off[r], lds + q0 * 8);
+    }
   }
 };
 

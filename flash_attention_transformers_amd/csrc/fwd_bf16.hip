@@ -9,11 +9,12 @@
 // Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
 //  * each wave owns 32 query rows and keeps them as the B operand of
 //    S^T = K Q^T in registers for the whole kernel (lane = query column);
-//  * K/V tiles of 64 keys are staged row-major through LDS (16-byte buffer
-//    loads, prefetched into registers one tile ahead); K rows are the A
-//    operand of S^T, and the A operand of O^T = V^T P^T is read transposed
-//    straight from the V tile with ds_read_b64_tr_b16, in the key order that
-//    P^T carries out of the S^T accumulator;
+//  * K/V tiles of 64 keys are copied straight from global memory into
+//    double-buffered LDS (buffer_load ... lds), one tile ahead, one barrier
+//    per tile; K rows are the A operand of S^T, and the A operand of
+//    O^T = V^T P^T is read transposed straight from the V tile with
+//    ds_read_b64_tr_b16, in the key order that P^T carries out of the S^T
+//    accumulator;
 //  * S^T lands with one query per lane, so the running row max and row sum
 //    are per-lane scalars: 32 in-lane values plus one exchange with lane^32;
 //  * P is rounded to bf16 and fed to the PV MFMA straight from registers;
@@ -33,8 +34,10 @@ constexpr int FWD_THREADS = 256;
 
 template <int D>
 struct FwdTile {
-  static constexpr int P = TilePitch<D>::value;                  // LDS row pitch (bf16)
-  static constexpr int CHUNKS = FWD_BN * D / 8 / FWD_THREADS;    // 16-byte chunks per thread per tensor
+  static constexpr int KP = RowPitch<D>::value;  // K tile: read as row operands
+  static constexpr int VP = TrPitch<D>::value;   // V tile: read transposed
+  using KTile = DirectTile<D, FWD_BN, KP, FWD_THREADS>;
+  using VTile = DirectTile<D, FWD_BN, VP, FWD_THREADS>;
 };
 
 template <int D, bool CAUSAL>
@@ -44,8 +47,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      float* __restrict__ LSE, int Hq, int G, int Sq, int Skv,
                      float c /* scale*log2(e) */, int n_qt) {
   using T = FwdTile<D>;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * T::P];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[FWD_BN * T::P];
+  // Double-buffered K and V tiles, filled straight from global memory.
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][FWD_BN * T::KP];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][FWD_BN * T::VP];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -55,9 +59,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int h = bh % Hq, b = bh / Hq;
   const int Hkv = Hq / G;
   const size_t kv_off = ((size_t)(b * Hkv + h / G) * Skv) * D;
+  const bf16* Kh = K + kv_off;
+  const bf16* Vh = V + kv_off;
   const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
-  const Buf kbuf(K + kv_off, (uint32_t)Skv * D * 2);
-  const Buf vbuf(V + kv_off, (uint32_t)Skv * D * 2);
 
   const int q0 = qt * FWD_BM;
   const int qw0 = q0 + wave * 32;          // first query of this wave
@@ -74,59 +78,60 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   if (CAUSAL) kv_end = min(Skv, q0 + FWD_BM + diag);
   const int n_kt = (kv_end + FWD_BN - 1) / FWD_BN;
 
-  // Register staging of one K/V tile (rows past Skv load as zeros).
-  uint4 kreg[T::CHUNKS], vreg[T::CHUNKS];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int r = 0; r < T::CHUNKS; ++r) {
-      const int ch = tid + FWD_THREADS * r;
-      const uint32_t off = (uint32_t)((j0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2;
-      kreg[r] = kbuf.ld16(off);
-      vreg[r] = vbuf.ld16(off);
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int r = 0; r < T::CHUNKS; ++r) {
-      const int ch = tid + FWD_THREADS * r;
-      const int o = (ch / (D / 8)) * T::P + (ch % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Ks[o]) = kreg[r];
-      *reinterpret_cast<uint4*>(&Vs[o]) = vreg[r];
-    }
+  typename T::KTile kt_ld;
+  typename T::VTile vt_ld;
+  kt_ld.init(tid);
+  vt_ld.init(tid);
+  // Tile j0: descriptors start at row j0 and end at Skv, so rows past the
+  // end (and pad slots) read as zeros.
+  auto issue_tile = [&](int j0, int buf) {
+    const uint32_t nb = (uint32_t)(Skv - j0) * D * 2;
+    kt_ld.load(Buf(Kh + (size_t)j0 * D, nb), Ks[buf], tid);
+    vt_ld.load(Buf(Vh + (size_t)j0 * D, nb), Vs[buf], tid);
   };
 
   f32x16 acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) acc[db] = zero_f32x16();
-  // Reference max of t = s*c for this query (shared by lane and lane^32) and
-  // this lane's partial row sum relative to it.  The reference only moves
-  // when a tile's max exceeds it by more than RESCALE_SLACK (log2 units), so
-  // most tiles skip the O rescale; p <= 2^RESCALE_SLACK stays well inside
-  // fp32/bf16 range and O / l is unchanged.
+  // Reference max of t = s*c for this lane's query (shared by lane and
+  // lane^32) and this lane's partial row sum relative to it.  The reference
+  // only moves when a tile's max exceeds it by more than RESCALE_SLACK (log2
+  // units), so most tiles skip the O rescale; p <= 2^RESCALE_SLACK stays well
+  // inside fp32/bf16 range and O / l is unchanged.
   constexpr float RESCALE_SLACK = 8.0f;
-  float m = -MATTN_INF;
-  float l = 0.f;
+  float m = -MATTN_INF, l = 0.f;
 
-  if (n_kt > 0) load_tile(0);
+  if (n_kt > 0) issue_tile(0, 0);
   for (int kt = 0; kt < n_kt; ++kt) {
-    const int j0 = kt * FWD_BN;
+    const int j0 = kt * FWD_BN, buf = kt & 1;
+    // This thread's copies of tile kt are done; after the barrier every
+    // thread's are, and every wave has finished reading tile kt-1, so the
+    // other buffer can be refilled.
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); lgkm and exp counters untouched
     __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(j0 + FWD_BN);
+    if (kt + 1 < n_kt) issue_tile(j0 + FWD_BN, buf ^ 1);
+    const bf16* Kb = Ks[buf];
+    const bf16* Vb = Vs[buf];
 
     // S^T for two 32-key blocks: lane = query column, regs = keys.
     f32x16 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) sc[kb] = zero_f32x16();
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st)
+    for (int st0 = 0; st0 < D / 16; st0 += 4) {
+      bf16x8 a[4][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sc[kb] = mfma32(ld_row_operand(Ks, T::P, kb * 32, 16 * st, lane), qf[st], sc[kb]);
-      }
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) a[u][kb] = ld_row_operand(Kb, T::KP, kb * 32, 16 * (st0 + u), lane);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(a[u][kb], qf[st0 + u], sc[kb]);
+    }
 
     const bool fast = !((j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag))) && c > 0.f;
+    bf16x8 pb[2][2];
     float mt;
     if (fast) {
       float mx = sc[0][0];
@@ -162,7 +167,6 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
     }
     const float m_use = (m == -MATTN_INF) ? 0.f : m;
-
     float rs = 0.f;
     if (fast) {
 #pragma unroll
@@ -170,8 +174,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = fast_exp2(__builtin_fmaf(sc[kb][i], c, -m_use));
-          sc[kb][i] = p;
           rs += p;
+          pb[kb][i >> 3][i & 7] = (bf16)p;
         }
     } else {
 #pragma unroll
@@ -179,35 +183,29 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float p = fast_exp2(sc[kb][i] - m_use);
-          sc[kb][i] = p;
           rs += p;
+          pb[kb][i >> 3][i & 7] = (bf16)p;
         }
     }
     l += rs;
-
-    bf16x8 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kb][t][e] = (bf16)sc[kb][8 * t + e];
 
     // O^T += V^T P^T.
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 a[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          acc[db] = mfma32(ld_trans_operand(Vs, T::P, kb * 32 + 16 * t, db * 32, lane),
-                           pb[kb][t], acc[db]);
-        }
+        for (int db = 0; db < D / 32; ++db)
+          a[db] = ld_trans_operand(Vb, T::VP, kb * 32 + 16 * t, db * 32, lane);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[kb][t], acc[db]);
+      }
   }
 
-  l += __shfl_xor(l, 32);
+  const float lt = l + __shfl_xor(l, 32);
   if (qrow < Sq) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     bf16* orow = O + ((size_t)bh * Sq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -220,7 +218,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         *reinterpret_cast<uint2*>(orow + d) = w;
       }
     if (g == 0)
-      LSE[(size_t)bh * Sq + qrow] = l > 0.f ? (m + log2f(l)) * MATTN_LN2 : -MATTN_INF;
+      LSE[(size_t)bh * Sq + qrow] = lt > 0.f ? (m + log2f(lt)) * MATTN_LN2 : -MATTN_INF;
   }
 }
 
