@@ -117,21 +117,33 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     f32x16 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) sc[kb] = zero_f32x16();
+    {
+      // All K fragments of the tile, issued ahead of the MFMAs that use them
+      // (eight reads in flight before the first MFMA, then one per MFMA).
+      bf16x8 a[D / 16][2];
 #pragma unroll
-    for (int st0 = 0; st0 < D / 16; st0 += 4) {
-      bf16x8 a[4][2];
+      for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int kb = 0; kb < 2; ++kb) a[st][kb] = ld_row_operand(Kb, T::KP, kb * 32, 16 * st, lane);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) a[u][kb] = ld_row_operand(Kb, T::KP, kb * 32, 16 * (st0 + u), lane);
+      for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+        for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(a[st][kb], qf[st], sc[kb]);
+      constexpr int NREAD = D / 16 * 2, AHEAD = 8;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(a[u][kb], qf[st0 + u], sc[kb]);
+      for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < NREAD - AHEAD; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
 
     const bool fast = !((j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag))) && c > 0.f;
     bf16x8 pb[2][2];
+    f32x16 tm[2];  // masked path: t = s*c, -inf where masked
     float mt;
     if (fast) {
       float mx = sc[0][0];
@@ -150,7 +162,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           const int key = j0 + kb * 32 + crow(i, g);
           const bool ok = key < Skv && (!CAUSAL || key <= qrow + diag);
           const float t = ok ? sc[kb][i] * c : -MATTN_INF;
-          sc[kb][i] = t;
+          tm[kb][i] = t;
           mx = fmaxf(mx, t);
         }
       mt = mx;
@@ -182,7 +194,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(sc[kb][i] - m_use);
+          const float p = fast_exp2(tm[kb][i] - m_use);
           rs += p;
           pb[kb][i >> 3][i & 7] = (bf16)p;
         }
