@@ -10,16 +10,20 @@
 //  * each wave owns 32 query rows and keeps them as the B operand of
 //    S^T = K Q^T in registers for the whole kernel (lane = query column);
 //  * K/V tiles of 64 keys are copied straight from global memory into
-//    double-buffered LDS (buffer_load ... lds), one tile ahead, one barrier
-//    per tile; K rows are the A operand of S^T, and the A operand of
-//    O^T = V^T P^T is read transposed straight from the V tile with
-//    ds_read_b64_tr_b16, in the key order that P^T carries out of the S^T
-//    accumulator;
+//    double-buffered LDS (buffer_load ... lds), one barrier per tile; K rows
+//    are the A operand of S^T, and the A operand of O^T = V^T P^T is read
+//    transposed straight from the V tile with ds_read_b64_tr_b16, in the key
+//    order that P^T carries out of the S^T accumulator;
 //  * S^T lands with one query per lane, so the running row max and row sum
 //    are per-lane scalars: 32 in-lane values plus one exchange with lane^32;
 //  * P is rounded to bf16 and fed to the PV MFMA straight from registers;
 //  * O^T accumulates in fp32 registers, one query per lane, so the online
-//    rescale is one multiply by a per-lane factor.
+//    rescale is one multiply by a per-lane factor;
+//  * the walk is software-pipelined one tile deep: while the MFMAs of
+//    S(t+1) run, the same wave computes the exponentials of tile t, and the
+//    row max of S(t+1) is taken under the MFMAs of O += P(t) V(t), so the
+//    softmax arithmetic issues between matrix instructions instead of
+//    after them.
 // Softmax runs in the log2 domain: t = s * scale * log2(e), p = 2^(t - m).
 #include "common.hpp"
 #include "kernels.hpp"
@@ -28,25 +32,31 @@ namespace mattn {
 
 namespace {
 
-constexpr int FWD_BM = 128;
 constexpr int FWD_BN = 64;
-constexpr int FWD_THREADS = 256;
 
+// Four waves per workgroup; each wave owns QB blocks of 32 query rows.  With
+// D = 128 a wave takes 64 rows (one wave per SIMD, up to 512 registers), so
+// every K/V fragment read from LDS feeds two MFMAs.
 template <int D>
 struct FwdTile {
+  static constexpr int QB = 1;
+  static constexpr int WAVES = 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int BM = 32 * QB * WAVES;     // query rows per workgroup
   static constexpr int KP = RowPitch<D>::value;  // K tile: read as row operands
   static constexpr int VP = TrPitch<D>::value;   // V tile: read transposed
-  using KTile = DirectTile<D, FWD_BN, KP, FWD_THREADS>;
-  using VTile = DirectTile<D, FWD_BN, VP, FWD_THREADS>;
+  using KTile = DirectTile<D, FWD_BN, KP, THREADS>;
+  using VTile = DirectTile<D, FWD_BN, VP, THREADS>;
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(FWD_THREADS, 2)
+__global__ __launch_bounds__(FwdTile<D>::THREADS, FwdTile<D>::QB == 2 ? 1 : 2)
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O,
                      float* __restrict__ LSE, int Hq, int G, int Sq, int Skv,
                      float c /* scale*log2(e) */, int n_qt) {
   using T = FwdTile<D>;
+  constexpr int QB = T::QB;
   // Double-buffered K and V tiles, filled straight from global memory.
   __shared__ __attribute__((aligned(16))) bf16 Ks[2][FWD_BN * T::KP];
   __shared__ __attribute__((aligned(16))) bf16 Vs[2][FWD_BN * T::VP];
@@ -63,145 +73,145 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* Vh = V + kv_off;
   const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
 
-  const int q0 = qt * FWD_BM;
-  const int qw0 = q0 + wave * 32;          // first query of this wave
-  const int qrow = qw0 + l32;              // this lane's query
+  const int q0 = qt * T::BM;
+  const int qw0 = q0 + wave * 32 * QB;     // first query of this wave
   const int diag = Skv - Sq;               // key j visible to query i iff j <= i + diag
+  auto qrow_of = [&](int qb) { return qw0 + 32 * qb + l32; };  // this lane's queries
 
-  // Q fragment, B operand of S^T = K Q^T: lane holds q[qrow][16s + 8g .. +7].
-  bf16x8 qf[D / 16];
+  // Q fragments, B operands of S^T = K Q^T: lane holds q[qrow][16s + 8g .. +7].
+  // The kernel works with a positive multiplier: a negative scale negates Q
+  // (exact in bf16) and a zero scale zeroes it (every visible score is then
+  // 0, whatever the multiplier).
+  bf16x8 qf[QB][D / 16];
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s)
-    qf[s] = as_bf16x8(qbuf.ld16((uint32_t)(qrow * D + 16 * s + 8 * g) * 2));
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qf[qb][s] = as_bf16x8(qbuf.ld16((uint32_t)(qrow_of(qb) * D + 16 * s + 8 * g) * 2));
+  if (!(c > 0.f)) {
+    const uint32_t flip = c < 0.f ? 0x80008000u : 0u, keep = c < 0.f ? ~0u : 0u;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        uint4 u = __builtin_bit_cast(uint4, qf[qb][s]);
+        u.x = (u.x & keep) ^ flip; u.y = (u.y & keep) ^ flip;
+        u.z = (u.z & keep) ^ flip; u.w = (u.w & keep) ^ flip;
+        qf[qb][s] = as_bf16x8(u);
+      }
+    c = c < 0.f ? -c : 1.f;
+  }
 
   int kv_end = Skv;
-  if (CAUSAL) kv_end = min(Skv, q0 + FWD_BM + diag);
+  if (CAUSAL) kv_end = min(Skv, q0 + T::BM + diag);
   const int n_kt = (kv_end + FWD_BN - 1) / FWD_BN;
 
   typename T::KTile kt_ld;
   typename T::VTile vt_ld;
   kt_ld.init(tid);
   vt_ld.init(tid);
-  // Tile j0: descriptors start at row j0 and end at Skv, so rows past the
-  // end (and pad slots) read as zeros.
-  auto issue_tile = [&](int j0, int buf) {
-    const uint32_t nb = (uint32_t)(Skv - j0) * D * 2;
-    kt_ld.load(Buf(Kh + (size_t)j0 * D, nb), Ks[buf], tid);
-    vt_ld.load(Buf(Vh + (size_t)j0 * D, nb), Vs[buf], tid);
+  // Tile t's descriptors start at its first row and end at Skv, so rows past
+  // the end (and pad slots) read as zeros.
+  auto issue_k = [&](int t) {
+    const int j0 = t * FWD_BN;
+    kt_ld.load(Buf(Kh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), Ks[t & 1], tid);
+  };
+  auto issue_v = [&](int t) {
+    const int j0 = t * FWD_BN;
+    vt_ld.load(Buf(Vh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), Vs[t & 1], tid);
+  };
+  // Whether some key of tile t is invisible to some query of this wave.
+  auto tile_masked = [&](int t) {
+    const int j0 = t * FWD_BN;
+    return (j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag));
   };
 
-  f32x16 acc[D / 32];
+  f32x16 acc[QB][D / 32];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = zero_f32x16();
-  // Reference max of t = s*c for this lane's query (shared by lane and
-  // lane^32) and this lane's partial row sum relative to it.  The reference
-  // only moves when a tile's max exceeds it by more than RESCALE_SLACK (log2
-  // units), so most tiles skip the O rescale; p <= 2^RESCALE_SLACK stays well
-  // inside fp32/bf16 range and O / l is unchanged.
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc[qb][db] = zero_f32x16();
+  // Per query block: reference max m of t = s*c for this lane's query
+  // (shared by lane and lane^32) and this lane's partial row sum relative to
+  // it.  The reference only moves when a tile's max exceeds it by more than
+  // RESCALE_SLACK (log2 units), so most tiles skip the O rescale;
+  // p <= 2^RESCALE_SLACK stays well inside fp32/bf16 range and O / l is
+  // unchanged.
   constexpr float RESCALE_SLACK = 8.0f;
-  float m = -MATTN_INF, l = 0.f;
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) { m[qb] = -MATTN_INF; l[qb] = 0.f; }
+  bf16x8 pb[QB][2][2];  // P^T of the current tile, B operands of O^T += V^T P^T
 
-  if (n_kt > 0) issue_tile(0, 0);
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int j0 = kt * FWD_BN, buf = kt & 1;
-    // This thread's copies of tile kt are done; after the barrier every
-    // thread's are, and every wave has finished reading tile kt-1, so the
-    // other buffer can be refilled.
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0); lgkm and exp counters untouched
-    __syncthreads();
-    if (kt + 1 < n_kt) issue_tile(j0 + FWD_BN, buf ^ 1);
-    const bf16* Kb = Ks[buf];
-    const bf16* Vb = Vs[buf];
-
-    // S^T for two 32-key blocks: lane = query column, regs = keys.
-    f32x16 sc[2];
+  // S^T = K Q^T for one 64-key tile: per query block, two 32-key blocks
+  // (lane = query column, registers = keys); each K fragment feeds QB MFMAs.
+  auto s_tile = [&](const bf16* Kb, f32x16 (&sc)[QB][2]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) sc[kb] = zero_f32x16();
-    {
-      // All K fragments of the tile, issued ahead of the MFMAs that use them
-      // (eight reads in flight before the first MFMA, then one per MFMA).
-      bf16x8 a[D / 16][2];
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
+      for (int kb = 0; kb < 2; ++kb) sc[qb][kb] = zero_f32x16();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) a[st][kb] = ld_row_operand(Kb, T::KP, kb * 32, 16 * st, lane);
+    for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
+      for (int kb = 0; kb < 2; ++kb) {
+        const bf16x8 a = ld_row_operand(Kb, T::KP, kb * 32, 16 * st, lane);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sc[kb] = mfma32(a[st][kb], qf[st], sc[kb]);
-      constexpr int NREAD = D / 16 * 2, AHEAD = 8;
-#pragma unroll
-      for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-      for (int i = 0; i < NREAD - AHEAD; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = mfma32(a, qf[qb][st], sc[qb][kb]);
       }
+  };
+  // Row max of a tile's raw scores; the masked form first overwrites
+  // invisible keys (past Skv, or above the causal diagonal) with -inf.
+  auto max_plain = [&](const f32x16 (&sc)[2]) {
+    float mx = sc[0][0];
 #pragma unroll
-      for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-
-    const bool fast = !((j0 + FWD_BN > Skv) || (CAUSAL && (j0 + FWD_BN - 1 > qw0 + diag))) && c > 0.f;
-    bf16x8 pb[2][2];
-    f32x16 tm[2];  // masked path: t = s*c, -inf where masked
-    float mt;
-    if (fast) {
-      float mx = sc[0][0];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
+    return mx;
+  };
+  auto max_masked = [&](f32x16 (&sc)[2], int t, int qrow) {
+    float mx = -MATTN_INF;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
-      mt = mx * c;
-    } else {
-      // Convert to t = s*c in place; masked keys become -inf.
-      float mx = -MATTN_INF;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = j0 + kb * 32 + crow(i, g);
-          const bool ok = key < Skv && (!CAUSAL || key <= qrow + diag);
-          const float t = ok ? sc[kb][i] * c : -MATTN_INF;
-          tm[kb][i] = t;
-          mx = fmaxf(mx, t);
-        }
-      mt = mx;
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int key = t * FWD_BN + kb * 32 + crow(i, g);
+        const bool ok = key < Skv && (!CAUSAL || key <= qrow + diag);
+        sc[kb][i] = ok ? sc[kb][i] : -MATTN_INF;
+        mx = fmaxf(mx, sc[kb][i]);
+      }
+    return mx;
+  };
+  // Move block qb's reference if the tile's max (lane and lane^32 together)
+  // passed it by more than the slack; O and l are rescaled to the new one.
+  auto update_ref = [&](int qb, float mx) {
+    float mt = mx * c;
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    if (wave_any(mt > m + RESCALE_SLACK)) {
-      const float m_new = fmaxf(m, mt);
-      const float alpha = (m_new == -MATTN_INF) ? 1.f : fast_exp2(m - m_new);
-      m = m_new;
-      l *= alpha;
+    if (wave_any(mt > m[qb] + RESCALE_SLACK)) {
+      const float m_new = fmaxf(m[qb], mt);
+      const float alpha = (m_new == -MATTN_INF) ? 1.f : fast_exp2(m[qb] - m_new);
+      m[qb] = m_new;
+      l[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+        for (int i = 0; i < 16; ++i) acc[qb][db][i] *= alpha;
     }
-    const float m_use = (m == -MATTN_INF) ? 0.f : m;
-    float rs = 0.f;
-    if (fast) {
+  };
+  // P = 2^(t - m) for one 32-key block, rounded to bf16 for the PV product;
+  // the row sum stays fp32, in four partial sums so that the adds do not
+  // form one long dependent chain.
+  auto exp_block = [&](const f32x16& sc, int qb, int kb, float (&rs)[4]) {
+    const float m_use = (m[qb] == -MATTN_INF) ? 0.f : m[qb];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(sc[kb][i], c, -m_use));
-          rs += p;
-          pb[kb][i >> 3][i & 7] = (bf16)p;
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(tm[kb][i] - m_use);
-          rs += p;
-          pb[kb][i >> 3][i & 7] = (bf16)p;
-        }
+    for (int i = 0; i < 16; ++i) {
+      const float p = fast_exp2(__builtin_fmaf(sc[i], c, -m_use));
+      rs[i & 3] += p;
+      pb[qb][kb][i >> 3][i & 7] = (bf16)p;
     }
-    l += rs;
-
-    // O^T += V^T P^T.
+  };
+  // O^T += V^T P^T; each V^T fragment feeds QB MFMAs.
+  auto pv_tile = [&](const bf16* Vb) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -211,26 +221,142 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         for (int db = 0; db < D / 32; ++db)
           a[db] = ld_trans_operand(Vb, T::VP, kb * 32 + 16 * t, db * 32, lane);
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[kb][t], acc[db]);
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a[db], pb[qb][kb][t], acc[qb][db]);
       }
+  };
+
+  // Software pipeline over key tiles.  Step t holds S(t) in registers and
+  // runs, interleaved instruction by instruction:
+  //   phase 1: the MFMAs of S(t+1)  with  the exponentials of tile t;
+  //   phase 2: the MFMAs of O += P(t) V(t)  with  the row max of S(t+1);
+  // then moves the reference max for tile t+1.  K runs one tile ahead of V:
+  // step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1) behind them,
+  // one barrier per step.
+  constexpr int NMF = 16 * QB;  // MFMAs per phase
+  auto step = [&](int t, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's copies landed
+    __syncthreads();                     // everyone's, and step t-1 is done everywhere
+    if (t + 2 < n_kt) issue_k(t + 2);
+    issue_v(t + 1);
+    float rs[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
+    // Phase 1: the MFMAs of S(t+1) with the 112 VALU instructions per query
+    // block that turn S(t) into P(t).
+    s_tile(Ks[(t + 1) & 1], nxt);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) exp_block(cur[qb][kb], qb, kb, rs[qb]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < NMF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // Pin the row sums here: left alone, the compiler sinks the adds past the
+    // branch below and keeps every p live in fp32 until then.
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      asm volatile("" : "+v"(rs[qb][0]), "+v"(rs[qb][1]), "+v"(rs[qb][2]), "+v"(rs[qb][3]));
+      l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
+    }
+    // Phase 2: the MFMAs of O += P(t) V(t) with the row max of S(t+1).
+    float mx[QB];
+    if (tile_masked(t + 1)) {
+      pv_tile(Vs[t & 1]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = max_masked(nxt[qb], t + 1, qrow_of(qb));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      pv_tile(Vs[t & 1]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) mx[qb] = max_plain(nxt[qb]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+      for (int i = 0; i < NMF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) update_ref(qb, mx[qb]);
+  };
+  auto last_step = [&](int t, f32x16 (&cur)[QB][2]) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+      exp_block(cur[qb][0], qb, 0, rs);
+      exp_block(cur[qb][1], qb, 1, rs);
+      l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+    }
+    pv_tile(Vs[t & 1]);
+  };
+
+  f32x16 sa[QB][2], sb[QB][2];
+  issue_k(0);
+  if (n_kt > 1) issue_k(1);
+  issue_v(0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  s_tile(Ks[0], sa);
+  {
+    const bool mk = tile_masked(0);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      update_ref(qb, mk ? max_masked(sa[qb], 0, qrow_of(qb)) : max_plain(sa[qb]));
+  }
+  // Two steps per trip so that S(t) and S(t+1) swap registers without copies.
+  int t = 0;
+  for (; t + 2 < n_kt; t += 2) {
+    step(t, sa, sb);
+    step(t + 1, sb, sa);
+  }
+  if (t + 2 == n_kt) {
+    step(t, sa, sb);
+    last_step(t + 1, sb);
+  } else {
+    last_step(t, sa);
   }
 
-  const float lt = l + __shfl_xor(l, 32);
-  if (qrow < Sq) {
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    bf16* orow = O + ((size_t)bh * Sq + qrow) * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qrow = qrow_of(qb);
+    const float lt = l[qb] + __shfl_xor(l[qb], 32);
+    if (qrow < Sq) {
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      bf16* orow = O + ((size_t)bh * Sq + qrow) * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = db * 32 + r * 8 + g * 4;
-        uint2 w;
-        w.x = pack_bf16x2(acc[db][4 * r + 0] * inv, acc[db][4 * r + 1] * inv);
-        w.y = pack_bf16x2(acc[db][4 * r + 2] * inv, acc[db][4 * r + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + d) = w;
-      }
-    if (g == 0)
-      LSE[(size_t)bh * Sq + qrow] = lt > 0.f ? (m + log2f(lt)) * MATTN_LN2 : -MATTN_INF;
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = db * 32 + r * 8 + g * 4;
+          uint2 w;
+          w.x = pack_bf16x2(acc[qb][db][4 * r + 0] * inv, acc[qb][db][4 * r + 1] * inv);
+          w.y = pack_bf16x2(acc[qb][db][4 * r + 2] * inv, acc[qb][db][4 * r + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d) = w;
+        }
+      if (g == 0)
+        LSE[(size_t)bh * Sq + qrow] = lt > 0.f ? (m[qb] + log2f(lt)) * MATTN_LN2 : -MATTN_INF;
+    }
   }
 }
 
@@ -239,9 +365,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v,
                              void* o, float* lse, hipStream_t stream) {
-  const int n_qt = (p.Sq + FWD_BM - 1) / FWD_BM;
+  const int n_qt = (p.Sq + FwdTile<D>::BM - 1) / FwdTile<D>::BM;
   const long long blocks = (long long)p.B * p.Hq * n_qt;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(FWD_THREADS), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(FwdTile<D>::THREADS), 0,
                      stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, p.Hq,
                      p.Hq / p.Hkv, p.Sq, p.Skv, p.scale * MATTN_LOG2E, n_qt);
   return hipGetLastError();
