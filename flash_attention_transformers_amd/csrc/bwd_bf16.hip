@@ -27,8 +27,9 @@
 //     and dO in registers and walks the K/V tiles:
 //        S^T = K Q^T, dP^T = V dO^T        (lane = query column)
 //        dQ^T += K^T dS^T
-// Q/dO and K/V tiles are staged row-major in LDS; every transposed MFMA
-// operand (dO^T, Q^T, K^T) is read with ds_read_b64_tr_b16.
+// Q/dO and K/V tiles are staged row-major in LDS, once each; every
+// transposed MFMA operand (dO^T, Q^T, K^T) is read from that copy with
+// ds_read_b64_tr_b16.
 #include <type_traits>
 
 #include "common.hpp"
@@ -90,14 +91,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      int nsplit, int q_chunk) {
   constexpr int BMQ = BWD_BMQ;            // query rows per step (two 32-row sub-blocks)
   constexpr int NSUB = BMQ / 32;
-  constexpr int RP = RowPitch<D>::value, TRP = TrPitch<D>::value;
+  constexpr int RP = RowPitch<D>::value;
   constexpr int CH = BMQ * D / 8 / DKDV_THREADS;  // 16-byte chunks per thread per tensor
   static_assert(CH >= 1 && (BMQ * D / 8) % DKDV_THREADS == 0, "tile loader must tile the workgroup");
-  // Q and dO tiles, each twice: row-operand pitch and transposed-read pitch.
+  // Q and dO tiles at the row-operand pitch; the transposed reads (dO^T,
+  // Q^T) use the same copy, which measured cheaper than storing a second copy
+  // at the transposed-read pitch.
   __shared__ __attribute__((aligned(16))) bf16 Qs[BMQ * RP];
   __shared__ __attribute__((aligned(16))) bf16 dOs[BMQ * RP];
-  __shared__ __attribute__((aligned(16))) bf16 Qt[BMQ * TRP];
-  __shared__ __attribute__((aligned(16))) bf16 dOt[BMQ * TRP];
   // P handed from each P-wave to its dS-wave: [slice][sub-block][blk][lane][4].
   __shared__ __attribute__((aligned(16))) float Pex[4 * NSUB * 4 * 64 * 4];
   __shared__ __attribute__((aligned(16))) float lse_s[BMQ];
@@ -182,8 +183,6 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
       *reinterpret_cast<uint4*>(&Qs[row * RP + col]) = qreg[r2];
       *reinterpret_cast<uint4*>(&dOs[row * RP + col]) = doreg[r2];
-      *reinterpret_cast<uint4*>(&Qt[row * TRP + col]) = qreg[r2];
-      *reinterpret_cast<uint4*>(&dOt[row * TRP + col]) = doreg[r2];
     }
     if (tid < BMQ) {
       // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
@@ -241,7 +240,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           bf16x8 a[D / 32];
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
-            a[db] = ld_trans_operand(dOt, TRP, qb * 32 + 16 * t, db * 32, lane);
+            a[db] = ld_trans_operand(dOs, RP, qb * 32 + 16 * t, db * 32, lane);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[qb][t], acc[db]);
         }
@@ -289,7 +288,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           bf16x8 a[D / 32];
 #pragma unroll
           for (int db = 0; db < D / 32; ++db)
-            a[db] = ld_trans_operand(Qt, TRP, qb * 32 + 16 * t, db * 32, lane);
+            a[db] = ld_trans_operand(Qs, RP, qb * 32 + 16 * t, db * 32, lane);
 #pragma unroll
           for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], dsb[t], acc[db]);
         }
@@ -371,18 +370,17 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const float* __restrict__ LSE, const float* __restrict__ DLT,
                    bf16* __restrict__ dQ, int Hq, int G, int Sq, int Skv, float scale, float c,
                    int n_qt) {
-  constexpr int RP = RowPitch<D>::value, TRP = TrPitch<D>::value;
+  constexpr int RP = RowPitch<D>::value;
   constexpr int CH = DQ_BN * D / 8 / DQ_THREADS;  // 16-byte chunks per thread per tensor
   static_assert(CH >= 1 && (DQ_BN * D / 8) % DQ_THREADS == 0, "tile loader must tile the workgroup");
-  // K (twice: row-operand and transposed-read pitch) and V tiles during the
-  // walk; afterwards the same LDS holds the key-half partials of dQ^T:
-  // [slice][db][r][lane][4] floats.
-  constexpr int TILE_BYTES = DQ_BN * (2 * RP + TRP) * 2;
+  // K and V tiles at the row-operand pitch during the walk (K^T is read
+  // transposed from the same K copy); afterwards the same LDS holds the
+  // key-half partials of dQ^T: [slice][db][r][lane][4] floats.
+  constexpr int TILE_BYTES = DQ_BN * 2 * RP * 2;
   constexpr int RED_BYTES = 4 * (D / 32) * 4 * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES];
   bf16* Ks = reinterpret_cast<bf16*>(smem);
   bf16* Vs = Ks + DQ_BN * RP;
-  bf16* Kt = Vs + DQ_BN * RP;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -440,7 +438,6 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       const int ch = tid + DQ_THREADS * r;
       const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
       *reinterpret_cast<uint4*>(&Ks[row * RP + col]) = kreg[r];
-      *reinterpret_cast<uint4*>(&Kt[row * TRP + col]) = kreg[r];
       *reinterpret_cast<uint4*>(&Vs[row * RP + col]) = vreg[r];
     }
     __syncthreads();
@@ -480,7 +477,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         bf16x8 a[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          a[db] = ld_trans_operand(Kt, TRP, kb0 + 16 * t, db * 32, lane);
+          a[db] = ld_trans_operand(Ks, RP, kb0 + 16 * t, db * 32, lane);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) adq[db] = mfma32(a[db], dsb[t], adq[db]);
       }

@@ -49,9 +49,11 @@ __device__ __forceinline__ constexpr int crow(int i, int g) {
 //   * transposed operands: 32 lanes read 64 bytes from each of 4 consecutive
 //     rows; pitch 320 B (D = 128) / 192 B (D = 64) puts the 4 rows in
 //     disjoint 64-byte bank segments.
-// No single pitch serves both, so a tile read both ways is stored twice.
-// Measured on MI355X: 197 (rows, 304 B) and 182 (transposed, 320 B) bytes per
-// clock per CU, against 62 and 116 with the pitches swapped.
+// No single pitch serves both.  Measured on MI355X: 197 (rows, 304 B) and 182
+// (transposed, 320 B) bytes per clock per CU, against 62 and 116 with the
+// pitches swapped.  A tile that is read both ways is still stored once, at
+// the row pitch: a second copy cost more LDS write traffic than the slower
+// transposed reads lose.
 template <int D>
 struct RowPitch {
   static constexpr int value = D == 128 ? 152 : 104;
