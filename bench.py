@@ -62,6 +62,13 @@ def _traffic_from_profile(kernel: str, workload: str):
     return float(m_b.group(1))
 
 
+def roofline_kernel(stage: str, dtype: str) -> str:
+    """Kernel name (as rocprofv3 and the profile summaries call it) of a stage."""
+    if dtype == "bf16":
+        return {"fwd": "fwd_bf16_kernel", "dkdv": "bwd_dkdv_kernel", "dq": "bwd_dq_kernel"}[stage]
+    return {"fwd": "fwd_f32_kernel", "dkdv": "dkdv_f32_kernel", "dq": "dq_f32_kernel"}[stage]
+
+
 def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "flash_attention_transformers_amd", "csrc")
     h = hashlib.sha256()
@@ -214,9 +221,7 @@ def main():
     F = fwd_flop
     per_launch = {"fwd": F, "dkdv": 2.0 * F, "dq": 1.5 * F}
     dom = max((n for n in names if n in per_launch), key=lambda n: kern_ms[n])
-    kname = {"fwd": "fwd", "dkdv": "bwd_dkdv", "dq": "bwd_dq"}[dom] + "_kernel"
-    if w.dtype != "bf16":
-        kname = {"fwd": "fwd_f32_kernel", "dkdv": "dkdv_f32_kernel", "dq": "dq_f32_kernel"}[dom]
+    kname = roofline_kernel(dom, w.dtype)
     achieved = per_launch[dom] / (kern_ms[dom] * 1e-3) / 1e12
     roofline = {
         "kernel": kname,

@@ -35,3 +35,14 @@ def test_credited_flops():
     assert w.fwd_flop() == 4 * 4 * 32 * 4096 * 4096 * 128 / 2
     assert w.bwd_flop() == 2.5 * w.fwd_flop()
     assert W.WORKLOADS["dit_self"].fwd_flop() == 4 * 10 * 32760 ** 2 * 128
+
+
+def test_bench_roofline_kernels_have_sources():
+    # Every kernel the bench line can name has a source entry, so a committed
+    # counter summary for it can be matched against the current source.
+    import bench
+
+    for dtype in ("bf16", "f32"):
+        for stage in ("fwd", "dkdv", "dq"):
+            assert bench.roofline_kernel(stage, dtype) in bench.KERNEL_SOURCES
+    assert bench.roofline_kernel("fwd", "bf16") == "fwd_bf16_kernel"
