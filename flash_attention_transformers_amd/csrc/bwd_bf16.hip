@@ -18,11 +18,13 @@
 //       dS-wave: dP = dO V^T, dS = P (dP - Dlt) with P from LDS,
 //                dK^T += Q^T dS
 //     (lane = key column; K or V of the slice stays in registers as the MFMA
-//     B operand).  The walk covers every query tile of every query head of
-//     the group, in ascending head order, summing in registers.  Shapes with
-//     few KV tiles (short cross-attention KV) split the query range into
-//     fixed chunks that write fp32 partials, summed afterwards in chunk order
-//     by a reduction kernel.
+//     B operand).  The dS-wave runs one query tile behind the P-wave, so the
+//     VALU work of one wave meets MFMA work of the other on their shared SIMD;
+//     Q/dO tiles are double-buffered in LDS.  The walk covers every query
+//     tile of every query head of the group, in ascending head order, summing
+//     in registers.  Shapes with few KV tiles (short cross-attention KV) split
+//     the query range into fixed chunks that write fp32 partials, summed
+//     afterwards in chunk order by a reduction kernel.
 //  3. dQ: one workgroup per 128 query rows; each wave keeps its 32 rows of Q
 //     and dO in registers and walks the K/V tiles:
 //        S^T = K Q^T, dP^T = V dO^T        (lane = query column)
@@ -80,6 +82,7 @@ void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
 // ----------------------------------------------------------------------------
 // 2. dK/dV
 constexpr int DKDV_THREADS = 512;  // 4 key slices x 2 roles
+constexpr int DKDV_NBUF = 2;       // Q/dO tiles: the current one and the next
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DKDV_THREADS)
@@ -94,15 +97,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   constexpr int RP = RowPitch<D>::value;
   constexpr int CH = BMQ * D / 8 / DKDV_THREADS;  // 16-byte chunks per thread per tensor
   static_assert(CH >= 1 && (BMQ * D / 8) % DKDV_THREADS == 0, "tile loader must tile the workgroup");
-  // Q and dO tiles at the row-operand pitch; the transposed reads (dO^T,
-  // Q^T) use the same copy, which measured cheaper than storing a second copy
-  // at the transposed-read pitch.
-  __shared__ __attribute__((aligned(16))) bf16 Qs[BMQ * RP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[BMQ * RP];
+  // Q and dO tiles at the row-operand pitch, double-buffered: step t reads
+  // tiles t and t+1.  The transposed reads (dO^T, Q^T) use the same copy.
+  __shared__ __attribute__((aligned(16))) bf16 Qs[DKDV_NBUF][BMQ * RP];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[DKDV_NBUF][BMQ * RP];
   // P handed from each P-wave to its dS-wave: [slice][sub-block][blk][lane][4].
   __shared__ __attribute__((aligned(16))) float Pex[4 * NSUB * 4 * 64 * 4];
-  __shared__ __attribute__((aligned(16))) float lse_s[BMQ];
-  __shared__ __attribute__((aligned(16))) float dlt_s[BMQ];
+  __shared__ __attribute__((aligned(16))) float lse_s[DKDV_NBUF][BMQ];
+  __shared__ __attribute__((aligned(16))) float dlt_s[DKDV_NBUF][BMQ];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -146,14 +148,15 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     if (first > q_lo) q_lo = (first / BMQ) * BMQ;
   }
   const int nq = qe > q_lo ? (qe - q_lo + BMQ - 1) / BMQ : 0;
-  const int n_it = G * nq;
+  const int n_it = G * nq;  // steps: query tiles of every head of the group, heads ascending
+  auto qt0_of = [&](int it) { return q_lo + (it % nq) * BMQ; };
 
   uint4 qreg[CH], doreg[CH];
   float pre_lse = 0.f, pre_dlt = 0.f;
   auto load_it = [&](int it) {
-    const int r = it / nq, qi = it - r * nq;
+    const int r = it / nq;
     const int h = kvh * G + r;
-    const int qt0 = q_lo + qi * BMQ;
+    const int qt0 = qt0_of(it);
     const size_t hoff = (size_t)(b * Hq + h) * Sq;
     // Rows at or past Sq fall outside the descriptors and load as zeros.
     const Buf qbuf(Q + hoff * D, (uint32_t)Sq * D * 2);
@@ -172,128 +175,160 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       pre_dlt = dbuf.ldf((uint32_t)(qt0 + tid) * 4);
     }
   };
-
-  if (n_it > 0) load_it(0);
-  for (int it = 0; it < n_it; ++it) {
-    const int qt0 = q_lo + (it % nq) * BMQ;
-    __syncthreads();
+  auto store_it = [&](int it, int buf) {
 #pragma unroll
     for (int r2 = 0; r2 < CH; ++r2) {
       const int ch = tid + DKDV_THREADS * r2;
       const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Qs[row * RP + col]) = qreg[r2];
-      *reinterpret_cast<uint4*>(&dOs[row * RP + col]) = doreg[r2];
+      *reinterpret_cast<uint4*>(&Qs[buf][row * RP + col]) = qreg[r2];
+      *reinterpret_cast<uint4*>(&dOs[buf][row * RP + col]) = doreg[r2];
     }
     if (tid < BMQ) {
       // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
-      const bool real = qt0 + tid < Sq;
-      lse_s[tid] = real ? pre_lse * MATTN_LOG2E : MATTN_INF;
-      dlt_s[tid] = real ? pre_dlt : 0.f;
+      const bool real = qt0_of(it) + tid < Sq;
+      lse_s[buf][tid] = real ? pre_lse * MATTN_LOG2E : MATTN_INF;
+      dlt_s[buf][tid] = real ? pre_dlt : 0.f;
     }
-    __syncthreads();
-    if (it + 1 < n_it) load_it(it + 1);
+  };
 
-    float* pex = Pex + slice * (NSUB * 4 * 64 * 4);
-    auto pwave_step = [&](auto masked) {
-      constexpr bool MASK = decltype(masked)::value;
-      // S = Q K^T (lane = key column, regs = query rows), both sub-blocks
-      // as independent MFMA chains over one batch of operand reads.
-      f32x16 sa[NSUB];
+  float* pex = Pex + slice * (NSUB * 4 * 64 * 4);
+  // S = Q K^T (P-wave) or dP = dO V^T (dS-wave) for one tile: lane = key
+  // column, registers = query rows; both sub-blocks as independent chains.
+  auto score_tile = [&](const bf16* tile, f32x16 (&sc)[NSUB]) {
 #pragma unroll
-      for (int qb = 0; qb < NSUB; ++qb) sa[qb] = zero_f32x16();
+    for (int qb = 0; qb < NSUB; ++qb) sc[qb] = zero_f32x16();
 #pragma unroll
-      for (int st0 = 0; st0 < D / 16; st0 += 4) {
-        bf16x8 a[NSUB][4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int qb = 0; qb < NSUB; ++qb)
-            a[qb][u] = ld_row_operand(Qs, RP, qb * 32, 16 * (st0 + u), lane);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int qb = 0; qb < NSUB; ++qb) sa[qb] = mfma32(a[qb][u], kvf[st0 + u], sa[qb]);
-      }
-      bf16x8 pb[NSUB][2];
+    for (int st = 0; st < D / 16; ++st)
 #pragma unroll
       for (int qb = 0; qb < NSUB; ++qb)
+        sc[qb] = mfma32(ld_row_operand(tile, RP, qb * 32, 16 * st, lane), kvf[st], sc[qb]);
+  };
+  // P = 2^(S*c - LSE*log2e), masked above the causal diagonal; P goes to
+  // the dS-wave through LDS and stays in registers as bf16 for dV.
+  bf16x8 pb[NSUB][2];
+  auto exp_tile = [&](auto masked, int buf, int qt0, const f32x16 (&sc)[NSUB]) {
+    constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          const f32x4 L = *reinterpret_cast<const f32x4*>(&lse_s[qb * 32 + 8 * blk + 4 * g]);
-          f32x4 pv;
+    for (int qb = 0; qb < NSUB; ++qb) {
+      // Register i holds query row qt0 + 32qb + 4g + (i/4)*8 + i%4; the key
+      // is above the diagonal for that row iff y exceeds the constant part.
+      const int y = key - diag - qt0 - qb * 32 - 4 * g;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * blk + j;
-            float pr = fast_exp2(__builtin_fmaf(sa[qb][i], c, -L[j]));
-            if (MASK && key > qt0 + qb * 32 + crow(i, g) + diag) pr = 0.f;
-            pv[j] = pr;
-            pb[qb][i >> 3][i & 7] = (bf16)pr;
-          }
-          *reinterpret_cast<f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]) = pv;
+      for (int blk = 0; blk < 4; ++blk) {
+        const f32x4 Lv = *reinterpret_cast<const f32x4*>(&lse_s[buf][qb * 32 + 8 * blk + 4 * g]);
+        f32x4 pv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * blk + j;
+          float pr = fast_exp2(__builtin_fmaf(sc[qb][i], c, -Lv[j]));
+          if (MASK && y > 8 * blk + j) pr = 0.f;
+          pv[j] = pr;
+          pb[qb][i >> 3][i & 7] = (bf16)pr;
         }
-      __syncthreads();
-      // dV^T += dO^T P.
-#pragma unroll
-      for (int qb = 0; qb < NSUB; ++qb)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 a[D / 32];
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            a[db] = ld_trans_operand(dOs, RP, qb * 32 + 16 * t, db * 32, lane);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[qb][t], acc[db]);
-        }
-    };
-    if (pwave) {
-      if (CAUSAL && (kw0 + 31 > qt0 + diag))
-        pwave_step(std::true_type{});
-      else
-        pwave_step(std::false_type{});
-    } else {
-      // dP = dO V^T, same layout as S.
-      f32x16 dp[NSUB];
-#pragma unroll
-      for (int qb = 0; qb < NSUB; ++qb) dp[qb] = zero_f32x16();
-#pragma unroll
-      for (int st0 = 0; st0 < D / 16; st0 += 4) {
-        bf16x8 a[NSUB][4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int qb = 0; qb < NSUB; ++qb)
-            a[qb][u] = ld_row_operand(dOs, RP, qb * 32, 16 * (st0 + u), lane);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int qb = 0; qb < NSUB; ++qb) dp[qb] = mfma32(a[qb][u], kvf[st0 + u], dp[qb]);
-      }
-      __syncthreads();
-      // dS = P (dP - Dlt); dK^T += Q^T dS.
-#pragma unroll
-      for (int qb = 0; qb < NSUB; ++qb) {
-        bf16x8 dsb[2];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[qb * 32 + 8 * blk + 4 * g]);
-          const f32x4 pv = *reinterpret_cast<const f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * blk + j;
-            dsb[i >> 3][i & 7] = (bf16)(pv[j] * (dp[qb][i] - Dl[j]));
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          bf16x8 a[D / 32];
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db)
-            a[db] = ld_trans_operand(Qs, RP, qb * 32 + 16 * t, db * 32, lane);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], dsb[t], acc[db]);
-        }
+        *reinterpret_cast<f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]) = pv;
       }
     }
+  };
+  // dV^T += dO^T P.
+  auto dv_tile = [&](int buf) {
+#pragma unroll
+    for (int qb = 0; qb < NSUB; ++qb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 a[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          a[db] = ld_trans_operand(dOs[buf], RP, qb * 32 + 16 * t, db * 32, lane);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[qb][t], acc[db]);
+      }
+  };
+  // dS = P (dP - Dlt), rounded to bf16 as the B operand of dK^T += Q^T dS.
+  auto ds_tile = [&](int buf, const f32x16 (&dp)[NSUB], bf16x8 (&dsb)[NSUB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < NSUB; ++qb)
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[buf][qb * 32 + 8 * blk + 4 * g]);
+        const f32x4 pv = *reinterpret_cast<const f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 4 * blk + j;
+          dsb[qb][i >> 3][i & 7] = (bf16)(pv[j] * (dp[qb][i] - Dl[j]));
+        }
+      }
+  };
+  auto dk_tile = [&](int buf, const bf16x8 (&dsb)[NSUB][2]) {
+#pragma unroll
+    for (int qb = 0; qb < NSUB; ++qb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 a[D / 32];
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+          a[db] = ld_trans_operand(Qs[buf], RP, qb * 32 + 16 * t, db * 32, lane);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], dsb[qb][t], acc[db]);
+      }
+  };
+
+  // The dS-wave runs one step behind the P-wave, so that on every SIMD (which
+  // holds the P-wave and the dS-wave of one slice) MFMA work of one wave
+  // meets VALU work of the other.  Step t, with tile t in buffer t&1 and tile
+  // t-1 in the other:
+  //   phase A: P-wave S(t) = Q K^T        | dS-wave dK^T += Q(t-1)^T dS(t-1)
+  //   phase B: P-wave P(t) = exp, to LDS  | dS-wave dP(t) = dO V^T
+  //   -- barrier: P(t) published --
+  //   phase C: P-wave dV^T += dO^T P(t)   | dS-wave dS(t) = P (dP - Dlt)
+  //            everyone stores tile t+1 (prefetched a step earlier) over
+  //            tile t-1, which phase A was the last to read
+  //   -- barrier: tile t+1 published --
+  // The buffer parity is a compile-time constant of each unrolled step.
+  f32x16 sc[NSUB];       // S(t) on the P-wave, dP(t) on the dS-wave
+  bf16x8 dsb[NSUB][2];   // dS(t-1), dS-wave only
+  auto step = [&](auto parity, int it) {
+    constexpr int b0 = decltype(parity)::value, b1 = b0 ^ 1;
+    if (pwave) {
+      score_tile(Qs[b0], sc);
+      const int qt0 = qt0_of(it);
+      if (CAUSAL && (kw0 + 31 > qt0 + diag))
+        exp_tile(std::true_type{}, b0, qt0, sc);
+      else
+        exp_tile(std::false_type{}, b0, qt0, sc);
+    } else {
+      if (it > 0) dk_tile(b1, dsb);
+      score_tile(dOs[b0], sc);
+    }
+    __syncthreads();  // P(it) is in Pex
+    if (it + 1 < n_it) {
+      store_it(it + 1, b1);
+      if (it + 2 < n_it) load_it(it + 2);
+    }
+    if (pwave)
+      dv_tile(b0);
+    else
+      ds_tile(b0, sc, dsb);
+    __syncthreads();  // tile it+1 is visible; Pex may be rewritten
+  };
+
+  if (n_it > 0) {
+    load_it(0);
+    store_it(0, 0);
+    if (n_it > 1) load_it(1);
+    __syncthreads();
+  }
+  int it = 0;
+  for (; it + 1 < n_it; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    step(std::integral_constant<int, 1>{}, it + 1);
+  }
+  if (it < n_it) step(std::integral_constant<int, 0>{}, it);
+  // The dS-wave's last dK uses the last tile, still in place.
+  if (!pwave && n_it > 0) {
+    if ((n_it - 1) & 1)
+      dk_tile(1, dsb);
+    else
+      dk_tile(0, dsb);
   }
 
   if (key >= Skv) return;
