@@ -12,3 +12,4 @@ from .attention import (  # noqa: F401
     probs_head,
     visible,
 )
+from .kvcache import gather_kv, kvcache_forward  # noqa: F401
