@@ -6,6 +6,7 @@ marshals arguments.  PyTorch supplies device memory and the current stream.
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=False, scale=None)
+    o, lse = fwd_kvcache(q, k_cache, v_cache, block_table, seqlens_k, causal=True)
 
 The ``mattn_*`` functions mirror the C entry points one to one and take
 pre-allocated tensors.  There is no fallback: if libmattn.so is missing or
@@ -54,6 +55,11 @@ def load_library() -> ctypes.CDLL:
     lib.mattn_bwd_stages.restype = i
     lib.mattn_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.mattn_bwd_workspace_size.restype = sz
+    lib.mattn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,
+                                      vp, sz, vp]
+    lib.mattn_fwd_kvcache.restype = i
+    lib.mattn_fwd_kvcache_workspace_size.argtypes = [i, i, i, i, i, i, i]
+    lib.mattn_fwd_kvcache_workspace_size.restype = sz
     lib.mattn_strerror.argtypes = [i]
     lib.mattn_strerror.restype = ctypes.c_char_p
     lib.mattn_version.argtypes = []
@@ -159,6 +165,59 @@ def mattn_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, workspace, stages: int,
                                          workspace.data_ptr(), nbytes, int(stages),
                                          _stream_handle(q, stream))
     _check(st)
+
+
+def mattn_fwd_kvcache_workspace_size(B: int, Hq: int, Hkv: int, Sq: int, D: int, page_size: int,
+                                     pages_per_seq: int) -> int:
+    return load_library().mattn_fwd_kvcache_workspace_size(B, Hq, Hkv, Sq, D, page_size,
+                                                           pages_per_seq)
+
+
+def mattn_fwd_kvcache(q, k_cache, v_cache, block_table, seqlens_k, o, lse, workspace,
+                      causal: bool = False, scale: Optional[float] = None, stream=None) -> None:
+    """Forward over a paged KV cache into pre-allocated o and lse.
+
+    q [B,Hq,Sq,D] bf16; k_cache/v_cache [num_pages,Hkv,page_size,D] bf16;
+    block_table [B,pages_per_seq] int32; seqlens_k [B] int32; workspace a
+    uint8 device tensor of at least mattn_fwd_kvcache_workspace_size() bytes
+    (or None when that is 0)."""
+    import torch
+
+    _require(q, k_cache, v_cache, block_table, seqlens_k, o, lse)
+    if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
+        raise TypeError("block_table and seqlens_k must be int32")
+    B, Hq, Sq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_cache.shape
+    pages_per_seq = block_table.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _require(workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    st = load_library().mattn_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                          block_table.data_ptr(), seqlens_k.data_ptr(),
+                                          o.data_ptr(), lse.data_ptr(), B, Hq, Hkv, Sq, D,
+                                          num_pages, page_size, pages_per_seq, int(causal),
+                                          float(scale), _dtype_code(q), ws_ptr, ws_bytes,
+                                          _stream_handle(q, stream))
+    _check(st)
+
+
+def fwd_kvcache(q, k_cache, v_cache, block_table, seqlens_k, causal: bool = False,
+                scale: Optional[float] = None, stream=None):
+    """Allocate and return (o, lse) of attention over a paged KV cache."""
+    import torch
+
+    B, Hq, Sq, D = q.shape
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device)
+    n = mattn_fwd_kvcache_workspace_size(B, Hq, k_cache.shape[1], Sq, D, k_cache.shape[2],
+                                         block_table.shape[1])
+    ws = torch.empty(n, dtype=torch.uint8, device=q.device) if n > 0 else None
+    mattn_fwd_kvcache(q, k_cache, v_cache, block_table, seqlens_k, o, lse, ws, causal, scale,
+                      stream)
+    return o, lse
 
 
 def fwd(q, k, v, causal: bool = False, scale: Optional[float] = None, stream=None):

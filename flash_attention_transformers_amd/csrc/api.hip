@@ -142,6 +142,50 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
                           MATTN_BWD_PREPROCESS | MATTN_BWD_DKDV | MATTN_BWD_DQ, stream);
 }
 
+size_t mattn_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Sq, int D, int page_size,
+                                        int pages_per_seq) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || page_size <= 0 || pages_per_seq <= 0 ||
+      Hq % Hkv != 0)
+    return 0;
+  mattn::KvCacheProblem p{B, Hq, Hkv, Sq, D, 0, 1.f, 1, page_size, pages_per_seq};
+  return mattn::kvcache_workspace_bytes(p);
+}
+
+mattn_status mattn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seqlens_k, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Sq, int D, int num_pages,
+                               int page_size, int pages_per_seq, int causal, float scale,
+                               mattn_dtype dtype, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (B < 0 || Hq < 0 || Hkv < 0 || Sq < 0 || D < 0 || num_pages < 0 || page_size <= 0 ||
+      pages_per_seq < 0)
+    return MATTN_ERR_INVALID_ARG;
+  if (Hkv == 0 || Hq % Hkv != 0) return MATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return MATTN_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return MATTN_ERR_INVALID_ARG;
+  if (dtype != MATTN_BF16 && dtype != MATTN_F32) return MATTN_ERR_INVALID_ARG;
+  if (dtype != MATTN_BF16) return MATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return MATTN_ERR_UNSUPPORTED;
+  if (page_size % 64 != 0) return MATTN_ERR_UNSUPPORTED;
+  const long long rows = (long long)B * Hq * Sq;
+  if (rows * D >= kMaxElems) return MATTN_ERR_UNSUPPORTED;
+  if ((long long)pages_per_seq * page_size >= kMaxElems) return MATTN_ERR_UNSUPPORTED;
+  if (rows == 0) return MATTN_OK;
+  if (!ptrs_ok({q, o, lse})) return MATTN_ERR_INVALID_ARG;
+  if (k_cache == nullptr || v_cache == nullptr || block_table == nullptr || seqlens_k == nullptr ||
+      !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)block_table & 3u) ||
+      ((uintptr_t)seqlens_k & 3u))
+    return MATTN_ERR_INVALID_ARG;
+  mattn::KvCacheProblem p{B, Hq, Hkv, Sq, D, causal, scale, num_pages, page_size, pages_per_seq};
+  const size_t need = mattn::kvcache_workspace_bytes(p);
+  if (need > 0 && (workspace == nullptr || !aligned16(workspace) || workspace_bytes < need))
+    return MATTN_ERR_INVALID_ARG;
+  if (mattn::launch_kvcache_bf16(p, q, k_cache, v_cache, block_table, seqlens_k, o, lse,
+                                 workspace, stream) != hipSuccess)
+    return MATTN_ERR_LAUNCH;
+  return MATTN_OK;
+}
+
 const char* mattn_strerror(mattn_status s) {
   switch (s) {
     case MATTN_OK: return "success";

@@ -42,6 +42,20 @@ hipError_t launch_dq_f32(const Problem& p, const float* q, const float* k, const
                          const float* lse, const float* dlt, const float* dout, float* dq,
                          hipStream_t stream);
 
+// Forward over a paged KV cache (kvcache_bf16.hip).
+struct KvCacheProblem {
+  int B, Hq, Hkv, Sq, D, causal;
+  float scale;
+  int num_pages, page_size, pages_per_seq;
+};
+// Number of key splits; depends only on the sizes.
+int kvcache_nsplit(const KvCacheProblem& p);
+// Workspace for the split partials (0 when there is one split).
+size_t kvcache_workspace_bytes(const KvCacheProblem& p);
+hipError_t launch_kvcache_bf16(const KvCacheProblem& p, const void* q, const void* kc,
+                               const void* vc, const int* block_table, const int* seqlens_k,
+                               void* o, float* lse, void* workspace, hipStream_t stream);
+
 // Zero-fill of n 4-byte words (used for dk/dv when there are no query rows).
 hipError_t launch_zero_words(void* p, size_t n_words, hipStream_t stream);
 

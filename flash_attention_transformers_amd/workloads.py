@@ -141,6 +141,102 @@ def to_torch(inp: Inputs, device) -> Dict[str, "object"]:
     return out
 
 
+@dataclasses.dataclass(frozen=True)
+class PagedWorkload:
+    """Queries against a paged KV cache: B sequences of effective key counts
+    ``seqlens``, each holding ceil(max(seqlens) / page_size) pages listed in a
+    shuffled block table (so neighbouring tokens of a sequence live in
+    scattered pages), plus ``extra_pages`` pages no sequence lists."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Sq: int
+    D: int
+    page_size: int
+    seqlens: Tuple[int, ...]
+    causal: bool
+    seed: int
+    extra_pages: int = 2
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def pages_per_seq(self) -> int:
+        return max(1, -(-max(self.seqlens) // self.page_size))
+
+    @property
+    def num_pages(self) -> int:
+        return self.B * self.pages_per_seq + self.extra_pages
+
+    def fwd_flop(self) -> float:
+        """Credited forward FLOP: 4*D per (query head, query, visible key),
+        counting the key rectangle Sq x L per sequence, halved when causal
+        and Sq > 1 (a decoded row sees every cached key)."""
+        pairs = sum(self.Sq * L for L in self.seqlens)
+        f = 4.0 * self.Hq * self.D * pairs
+        return f / 2 if (self.causal and self.Sq > 1) else f
+
+    def kv_bytes(self) -> float:
+        """K and V bytes of the effective lengths (bf16): what a single pass
+        has to read from HBM."""
+        return 2.0 * 2 * self.Hkv * self.D * sum(self.seqlens)
+
+
+def _seqlens(n: int, lo: int, hi: int, seed: int) -> Tuple[int, ...]:
+    r = np.random.default_rng(seed)
+    return tuple(int(x) for x in r.integers(lo, hi + 1, size=n))
+
+
+# Decode against KV caches whose effective lengths span the pages' KV growth
+# (4680 to 28080 keys per sequence, LingBot report, per-chunk work table),
+# grouped KV heads as in the xtrain decoder (row T15).
+PAGED_WORKLOADS: Dict[str, PagedWorkload] = {
+    w.name: w
+    for w in [
+        PagedWorkload("decode_paged", 8, 32, 8, 1, 128, 64, _seqlens(8, 4680, 28080, 61), True, 62),
+    ]
+}
+
+
+@dataclasses.dataclass
+class PagedInputs:
+    workload: PagedWorkload
+    vals: Dict[str, np.ndarray]       # q, k_cache, v_cache: float32 with the bf16 values
+    bits: Dict[str, np.ndarray]       # the same as bf16 bit patterns (uint16)
+    block_table: np.ndarray           # [B, pages_per_seq] int32
+    seqlens: np.ndarray               # [B] int32
+
+
+def make_paged_inputs(w: PagedWorkload) -> PagedInputs:
+    """PCG64(seed): standard_normal float32 drawn in the order q, k_cache,
+    v_cache, rounded to bf16 (RNE); then a permutation of the page ids, whose
+    first B * pages_per_seq entries form the block table row by row."""
+    rng = np.random.default_rng(w.seed)
+    shapes = {"q": (w.B, w.Hq, w.Sq, w.D),
+              "k_cache": (w.num_pages, w.Hkv, w.page_size, w.D),
+              "v_cache": (w.num_pages, w.Hkv, w.page_size, w.D)}
+    bits = {}
+    for n in ("q", "k_cache", "v_cache"):
+        bits[n] = round_to_bf16_bits(rng.standard_normal(shapes[n], dtype=np.float32))
+    vals = {n: bf16_bits_to_f32(b) for n, b in bits.items()}
+    perm = rng.permutation(w.num_pages).astype(np.int32)
+    bt = np.ascontiguousarray(perm[:w.B * w.pages_per_seq].reshape(w.B, w.pages_per_seq))
+    return PagedInputs(w, vals, bits, bt, np.asarray(w.seqlens, dtype=np.int32))
+
+
+def paged_to_torch(inp: PagedInputs, device) -> Dict[str, "object"]:
+    import torch
+
+    out = {n: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(device).contiguous()
+           for n, b in inp.bits.items()}
+    out["block_table"] = torch.from_numpy(inp.block_table).to(device).contiguous()
+    out["seqlens"] = torch.from_numpy(inp.seqlens).to(device).contiguous()
+    return out
+
+
 def head_sample(w: Workload, n: int, seed: int = 0) -> Tuple[Tuple[int, int], ...]:
     """A fixed, seeded choice of (b, h) pairs, always including the first and
     the last head."""

@@ -112,6 +112,52 @@ mattn_status mattn_bwd_stages(const void* q, const void* k, const void* v, const
                               float scale, mattn_dtype dtype, void* workspace,
                               size_t workspace_bytes, unsigned stages, hipStream_t stream);
 
+/* Forward attention over a paged KV cache: decode (Sq = 1..16 new tokens per
+ * sequence) and chunked prefill against cached keys.
+ *
+ * Defining passages: the LingBot report (same-card FA2/FA3 counter section
+ * and the per-call effective-length supplement) on attending to the
+ * effective K/V length recorded in cu_seqlens rather than the allocated
+ * buffer, and the xtrain evolution page (decode engine, milestone M2a) on one
+ * decoded token being the last row of causal attention.
+ *
+ * Layout (all row-major):
+ *   q, o         [B, Hq, Sq, D]                     bf16
+ *   lse          [B, Hq, Sq]                        float32, natural log
+ *   k_cache,
+ *   v_cache      [num_pages, Hkv, page_size, D]     bf16
+ *   block_table  [B, pages_per_seq]                 int32, page ids in token order
+ *   seqlens_k    [B]                                int32, effective key count
+ * Sequence b attends to the first seqlens_k[b] tokens of its pages (values are
+ * clamped to [0, pages_per_seq*page_size]); with causal = 1, query i sees key
+ * j iff j <= i + seqlens_k[b] - Sq (bottom-right).  Rows that see no key get
+ * o = 0 and lse = -inf.  Tokens past a sequence's length and pages it does
+ * not list are never read; a page id outside [0, num_pages) reads as zeros
+ * (no fault; that sequence's result is then meaningless).
+ *
+ * Sizes: bf16 only (MATTN_F32 returns MATTN_ERR_UNSUPPORTED); D in {64, 128};
+ * page_size a positive multiple of 64; Hq a multiple of Hkv.
+ * Workspace: caller-owned device memory of at least
+ * mattn_fwd_kvcache_workspace_size() bytes (0 is allowed when that is 0)
+ * holding the float32 partials of long caches split along the keys; the
+ * splits are merged in a fixed order, so results are bitwise reproducible.
+ * Every pointer is device memory owned by the caller; q, k_cache, v_cache, o,
+ * lse and workspace must be 16-byte aligned, the int32 arrays 4-byte
+ * aligned.  Errors are reported before anything is enqueued: null or
+ * misaligned pointers, negative sizes, Hq % Hkv != 0, causal not 0/1, a
+ * non-finite scale or too small a workspace give MATTN_ERR_INVALID_ARG;
+ * unsupported dtype, D or page size, or element counts of 2^31 or more give
+ * MATTN_ERR_UNSUPPORTED.  B*Hq*Sq == 0 is a no-op.  Enqueues one kernel, plus
+ * a merge kernel when the keys are split, on `stream`. */
+size_t mattn_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Sq, int D, int page_size,
+                                        int pages_per_seq);
+mattn_status mattn_fwd_kvcache(const void* q, const void* k_cache, const void* v_cache,
+                               const int* block_table, const int* seqlens_k, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Sq, int D, int num_pages,
+                               int page_size, int pages_per_seq, int causal, float scale,
+                               mattn_dtype dtype, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* mattn_strerror(mattn_status s);
 

@@ -27,7 +27,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["mattn_fwd", "mattn_bwd", "mattn_bwd_stages", "mattn_bwd_workspace_size", "mattn_strerror",
-         "mattn_version"])
+         "mattn_version", "mattn_fwd_kvcache", "mattn_fwd_kvcache_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -133,3 +133,54 @@ def test_bwd_stages_validates_like_bwd():
     st = lib.mattn_bwd_stages(P, P, P, P, P, P, P, P, P, 1, 2, 2, 128, 128, 96, 0, 0.125, 0, P,
                               1 << 40, fa.MATTN_BWD_DKDV, None)
     assert st == fa.MATTN_ERR_UNSUPPORTED
+
+
+def kc_status(q=P, kc=P, vc=P, bt=P, sl=P, o=P, lse=P, B=1, Hq=8, Hkv=8, Sq=1, D=128, num_pages=100,
+              page_size=64, pps=100, causal=1, scale=0.088, dtype=0, ws=P, ws_bytes=1 << 40):
+    lib = fa.load_library()
+    return lib.mattn_fwd_kvcache(q, kc, vc, bt, sl, o, lse, B, Hq, Hkv, Sq, D, num_pages, page_size,
+                                 pps, causal, scale, dtype, ws, ws_bytes, None)
+
+
+KC_INVALID = [
+    dict(B=-1), dict(Sq=-1), dict(Hkv=0), dict(Hq=6, Hkv=4), dict(causal=2), dict(page_size=0),
+    dict(pps=-1), dict(num_pages=-2), dict(scale=float("nan")), dict(dtype=5), dict(q=0),
+    dict(o=P + 8), dict(kc=0), dict(vc=P + 4), dict(bt=0), dict(sl=P + 2), dict(ws=0),
+    dict(ws_bytes=100),
+]
+
+
+@pytest.mark.parametrize("kw", KC_INVALID)
+def test_kvcache_rejects_invalid(kw):
+    # every case fails validation, so nothing is launched on the fake pointers
+    assert kc_status(**kw) == fa.MATTN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(dtype=1), dict(D=96), dict(page_size=48), dict(page_size=100),
+                                dict(B=1 << 14, Hq=1 << 10, Hkv=1 << 10, Sq=1)])
+def test_kvcache_rejects_unsupported(kw):
+    assert kc_status(**kw) == fa.MATTN_ERR_UNSUPPORTED
+
+
+def test_kvcache_empty_is_a_noop():
+    assert kc_status(B=0, q=0, o=0, lse=0, kc=0, vc=0, bt=0, sl=0, ws=0, ws_bytes=0) == fa.MATTN_OK
+    assert kc_status(Sq=0, ws=0, ws_bytes=0) == fa.MATTN_OK
+
+
+def test_kvcache_workspace_size():
+    ws = fa.mattn_fwd_kvcache_workspace_size
+    assert ws(0, 8, 8, 1, 128, 64, 100) == 0
+    assert ws(1, 6, 4, 1, 128, 64, 100) == 0
+    # many sequences x heads: one split, no workspace
+    assert ws(64, 32, 8, 1, 128, 64, 8) == 0
+    # one short batch over a long cache: split along the keys
+    n = ws(1, 8, 8, 1, 128, 64, 100)
+    rows = 8
+    assert n > 0 and n == ws(1, 8, 8, 1, 128, 64, 100)
+    ns = None
+    for cand in range(2, 65):
+        o_b = (cand * rows * 128 * 4 + 255) // 256 * 256
+        l_b = (cand * rows * 4 + 255) // 256 * 256
+        if o_b + l_b == n:
+            ns = cand
+    assert ns is not None and ns <= 25  # at least four 64-token tiles per split

@@ -1,0 +1,148 @@
+"""GPU parity of the paged-KV-cache forward against the float64 oracle, plus
+its behaviour: poisoned unused pages and tails, determinism, and agreement
+with the dense forward.  All calls go through the C ABI."""
+import numpy as np
+import pytest
+
+import flash_attention_transformers_amd as fa
+import oracle
+from flash_attention_transformers_amd import workloads as W
+
+import harness as H
+
+pytestmark = pytest.mark.gpu
+
+TOL = H.TOL["bf16"]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    fa.load_library()
+    return torch.device("cuda:0")
+
+
+def run(t, causal, scale=None):
+    import torch
+
+    o, lse = fa.fwd_kvcache(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seqlens"],
+                            causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def compare(w, inp, o, lse, seqs=None):
+    v = inp.vals
+    seqs = range(w.B) if seqs is None else seqs
+    for b in seqs:
+        ro, rl = oracle.kvcache_forward(v["q"][b:b + 1], v["k_cache"], v["v_cache"],
+                                        inp.block_table[b:b + 1], inp.seqlens[b:b + 1],
+                                        w.causal, w.scale)
+        go = H.to_np(o[b:b + 1])
+        gl = lse[b:b + 1].cpu().numpy().astype(np.float64)
+        # rows that see no key: O exactly 0 and LSE exactly -inf
+        none = np.isneginf(rl)
+        assert np.array_equal(np.isneginf(gl), none), b
+        assert np.all(go[none] == 0), b
+        fin = ~none
+        res = dict(b=b, o_max_abs=H.max_abs(go, ro), o_rel_l2=H.rel_l2(go, ro),
+                   lse_max_abs=H.max_abs(gl[fin], rl[fin]) if fin.any() else 0.0)
+        H.say(f"    {res}")
+        assert res["o_max_abs"] <= TOL["o_max_abs"], res
+        assert res["o_rel_l2"] <= TOL["o_rel_l2"], res
+        assert res["lse_max_abs"] <= TOL["lse_max_abs"], res
+
+
+# (name, B, Hq, Hkv, Sq, D, page_size, seqlens, causal)
+CASES = [
+    ("decode_gqa_split", 4, 8, 2, 1, 128, 64, (1, 64, 200, 384), True),
+    ("decode_mha_d64", 3, 4, 4, 1, 64, 128, (0, 77, 512), False),
+    ("prefill_chunk", 2, 4, 2, 16, 128, 64, (16, 500), True),
+    ("rows_without_keys", 1, 2, 1, 8, 128, 64, (5,), True),
+    ("many_splits", 1, 8, 8, 1, 128, 64, (6300,), True),
+    ("page128_offsets", 2, 4, 1, 4, 128, 128, (300, 640), True),
+    ("two_query_chunks", 1, 32, 2, 16, 64, 64, (250,), True),
+    ("noncausal_prefill_d64", 2, 6, 3, 5, 64, 64, (3, 129), False),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(CASES)), ids=[c[0] for c in CASES])
+def test_kvcache_parity(idx, dev):
+    name, B, Hq, Hkv, Sq, D, ps, lens, causal = CASES[idx]
+    w = W.PagedWorkload(name, B, Hq, Hkv, Sq, D, ps, lens, causal, seed=100 + idx)
+    H.say(f"[kvcache parity] {w}")
+    inp = W.make_paged_inputs(w)
+    t = W.paged_to_torch(inp, dev)
+    o, lse = run(t, causal)
+    compare(w, inp, o, lse)
+
+
+def test_unused_pages_and_tails_are_never_read(dev):
+    import torch
+
+    w = W.PagedWorkload("poison", 3, 8, 2, 2, 128, 64, (100, 7, 257), True, seed=31, extra_pages=5)
+    H.say(f"[kvcache poison] {w}")
+    inp = W.make_paged_inputs(w)
+    t = W.paged_to_torch(inp, dev)
+    o_clean, l_clean = run(t, True)
+    kc, vc = t["k_cache"].clone(), t["v_cache"].clone()
+    used = set()
+    for b, L in enumerate(w.seqlens):
+        for tok in range(L, w.pages_per_seq * w.page_size):
+            p = int(inp.block_table[b, tok // w.page_size])
+            kc[p, :, tok % w.page_size] = float("nan")
+            vc[p, :, tok % w.page_size] = float("nan")
+        used.update(int(p) for p in inp.block_table[b, : -(-L // w.page_size)])
+    for p in range(w.num_pages):
+        if p not in used:
+            kc[p] = float("nan")
+            vc[p] = float("inf")
+    t2 = dict(t, k_cache=kc, v_cache=vc)
+    o, lse = run(t2, True)
+    assert torch.equal(o.view(torch.int16), o_clean.view(torch.int16))
+    assert torch.equal(lse, l_clean)
+
+
+def test_kvcache_deterministic(dev):
+    import torch
+
+    w = W.PagedWorkload("det", 2, 8, 8, 1, 128, 64, (3000, 4100), True, seed=33)
+    inp = W.make_paged_inputs(w)
+    t = W.paged_to_torch(inp, dev)
+    a = run(t, True)
+    b = run(t, True)
+    assert torch.equal(a[0].view(torch.int16), b[0].view(torch.int16))
+    assert torch.equal(a[1], b[1])
+
+
+def test_kvcache_matches_dense_forward(dev):
+    # Identity block table and full lengths: the cache is just a reshaped
+    # dense K/V, so the paged result must agree with mattn_fwd.
+    import torch
+
+    B, Hq, Hkv, S, D, ps = 2, 8, 2, 256, 128, 64
+    w = W.Workload("dense_ref", B, Hq, Hkv, S, S, D, True, "bf16", 35, False)
+    t = W.to_torch(W.make_inputs(w), dev)
+    o_d, l_d = fa.fwd(t["q"], t["k"], t["v"], causal=True)
+    pps = S // ps
+    kc = t["k"].view(B, Hkv, pps, ps, D).permute(0, 2, 1, 3, 4).reshape(B * pps, Hkv, ps, D).contiguous()
+    vc = t["v"].view(B, Hkv, pps, ps, D).permute(0, 2, 1, 3, 4).reshape(B * pps, Hkv, ps, D).contiguous()
+    bt = torch.arange(B * pps, dtype=torch.int32, device=dev).view(B, pps).contiguous()
+    sl = torch.full((B,), S, dtype=torch.int32, device=dev)
+    o, lse = fa.fwd_kvcache(t["q"], kc, vc, bt, sl, causal=True)
+    torch.cuda.synchronize()
+    assert H.max_abs(H.to_np(o), H.to_np(o_d)) <= 2e-2
+    assert H.max_abs(lse.cpu().numpy(), l_d.cpu().numpy()) <= 1e-3
+
+
+def test_decode_paged_workload_sampled(dev):
+    # The benchmark's decode workload at full size, checked on two sequences.
+    w = W.PAGED_WORKLOADS["decode_paged"]
+    H.say(f"[kvcache sampled] {w}")
+    inp = W.make_paged_inputs(w)
+    t = W.paged_to_torch(inp, dev)
+    o, lse = run(t, w.causal)
+    compare(w, inp, o, lse, seqs=(0, w.B - 1))
