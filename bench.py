@@ -25,6 +25,7 @@ against the 2.5F credited to the backward.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -44,7 +45,9 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel": "fwd_bf16.hip", "bwd_dkdv_kernel": "bwd_bf16.hip",
     "bwd_dq_kernel": "bwd_bf16.hip", "fwd_f32_kernel": "attn_f32.hip",
     "dkdv_f32_kernel": "attn_f32.hip", "dq_f32_kernel": "attn_f32.hip",
+    "kvcache_fwd_kernel": "kvcache_bf16.hip",
 }
+HBM_PEAK_GBS = 8000.0
 
 
 def _traffic_from_profile(kernel: str, workload: str):
@@ -139,6 +142,128 @@ def cpu_baseline(w, budget_s: float = 12.0):
     }
 
 
+def cpu_baseline_paged(w, budget_s: float = 12.0):
+    """The paged oracle on the host cores, one whole sequence at a time (all
+    its query heads), until the time budget is spent."""
+    import oracle
+    from flash_attention_transformers_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    inp = W.make_paged_inputs(w)
+    v = inp.vals
+    done, flop = 0, 0.0
+    t0 = time.perf_counter()
+    while done < w.B:
+        b = done
+        oracle.kvcache_forward(v["q"][b:b + 1], v["k_cache"], v["v_cache"],
+                               inp.block_table[b:b + 1], inp.seqlens[b:b + 1], w.causal, w.scale)
+        one = dataclasses.replace(w, B=1, seqlens=(w.seqlens[b],))
+        flop += one.fwd_flop()
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {
+        "value": flop / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B} sequences (all {w.Hq} query heads, Sq={w.Sq}, their effective "
+                  f"cached keys), forward, float64, {el:.1f} s; rate credited like the GPU",
+    }
+
+
+def main_paged(args, w):
+    """Forward over the paged KV cache: one mattn_fwd_kvcache call per step
+    (the attention kernel plus, for split caches, the merge kernel)."""
+    import torch
+
+    import flash_attention_transformers_amd as fa
+    from flash_attention_transformers_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    fa.load_library()
+    inp = W.make_paged_inputs(w)
+    t = W.paged_to_torch(inp, dev)
+    del inp
+    q = t["q"]
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    n = fa.mattn_fwd_kvcache_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.D, w.page_size,
+                                            w.pages_per_seq)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev) if n > 0 else None
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.mattn_fwd_kvcache(q, t["k_cache"], t["v_cache"], t["block_table"], t["seqlens"], o, lse,
+                             ws, w.causal, w.scale, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    call_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    flop = w.fwd_flop()
+    value = flop / (ms_step * 1e-3) / 1e12
+    qo_bytes = 2.0 * 2 * w.B * w.Hq * w.Sq * w.D + 4.0 * w.B * w.Hq * w.Sq
+    moved = w.kv_bytes() + qo_bytes
+    achieved = moved / (call_ms * 1e-3) / 1e9
+    line = {
+        "metric": "attention TFLOPS fwd and fwd+bwd at 1 MI355X; % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) paged cache, shuffled block table, resident in HBM)",
+        "config": {
+            "workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Sq={w.Sq} D={w.D} "
+                        f"page_size={w.page_size} seqlens={list(w.seqlens)} causal={int(w.causal)}; "
+                        f"step = forward over the paged KV cache",
+            "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * value / BF16_PEAK_TFLOPS, 3),
+        "kernel_ms": {"kvcache": round(call_ms, 4)},
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {
+            "kernel": "kvcache_fwd_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": _traffic_from_profile("kvcache_fwd_kernel", w.name),
+            "bytes_per_launch": moved,
+        },
+    }
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline_paged(w)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +286,9 @@ def main():
     import flash_attention_transformers_amd as fa
     from flash_attention_transformers_amd import workloads as W
 
+    if args.workload in W.PAGED_WORKLOADS:
+        main_paged(args, W.PAGED_WORKLOADS[args.workload])
+        return
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     fa.load_library()
