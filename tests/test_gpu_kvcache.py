@@ -146,3 +146,34 @@ def test_decode_paged_workload_sampled(dev):
     t = W.paged_to_torch(inp, dev)
     o, lse = run(t, w.causal)
     compare(w, inp, o, lse, seqs=(0, w.B - 1))
+
+
+def test_bad_page_ids_and_lengths_do_not_fault(dev):
+    # Page ids outside [0, num_pages) read as zeros through an empty
+    # descriptor, lengths are clamped to the table's capacity (negative ones
+    # to 0); the other sequences are unaffected.
+    import torch
+
+    w = W.PagedWorkload("badmeta", 3, 4, 2, 1, 128, 64, (200, 150, 120), True, seed=41)
+    inp = W.make_paged_inputs(w)
+    t = W.paged_to_torch(inp, dev)
+    o_ref, l_ref = run(t, True)
+    bt = t["block_table"].clone()
+    bt[1, 0] = -1
+    bt[1, 1] = w.num_pages + 5
+    sl = t["seqlens"].clone()
+    sl[2] = -7
+    t2 = dict(t, block_table=bt, seqlens=sl)
+    o, lse = run(t2, True)
+    assert torch.equal(o[0].view(torch.int16), o_ref[0].view(torch.int16))
+    assert torch.equal(lse[0], l_ref[0])
+    assert torch.isfinite(o[1].float()).all()
+    assert (o[2].float() == 0).all() and torch.isneginf(lse[2]).all()
+    # a length beyond the table's capacity is clamped to it
+    sl3 = t["seqlens"].clone()
+    sl3[0] = 10 ** 6
+    o3, l3 = run(dict(t, seqlens=sl3), True)
+    v = inp.vals
+    ro, rl = oracle.kvcache_forward(v["q"][:1], v["k_cache"], v["v_cache"], inp.block_table[:1],
+                                    [w.pages_per_seq * 64], True, w.scale)
+    assert H.max_abs(H.to_np(o3[:1]), ro) <= TOL["o_max_abs"]
