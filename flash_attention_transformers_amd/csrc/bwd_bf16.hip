@@ -25,10 +25,13 @@
 //     in registers.  Shapes with few KV tiles (short cross-attention KV) split
 //     the query range into fixed chunks that write fp32 partials, summed
 //     afterwards in chunk order by a reduction kernel.
-//  3. dQ: one workgroup per 128 query rows; each wave keeps its 32 rows of Q
-//     and dO in registers and walks the K/V tiles:
+//  3. dQ: one workgroup per 128 query rows, 8 waves: four 32-row slices,
+//     each served by two waves that take the two 32-key halves of every
+//     64-key tile.  A wave keeps its 32 rows of Q and dO in registers and
+//     walks the K/V tiles:
 //        S^T = K Q^T, dP^T = V dO^T        (lane = query column)
 //        dQ^T += K^T dS^T
+//     and the two key-half partials are summed in a fixed order at the end.
 // Q/dO and K/V tiles are staged row-major in LDS, once each; every
 // transposed MFMA operand (dO^T, Q^T, K^T) is read from that copy with
 // ds_read_b64_tr_b16.

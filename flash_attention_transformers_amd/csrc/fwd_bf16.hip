@@ -34,9 +34,10 @@ namespace {
 
 constexpr int FWD_BN = 64;
 
-// Four waves per workgroup; each wave owns QB blocks of 32 query rows.  With
-// D = 128 a wave takes 64 rows (one wave per SIMD, up to 512 registers), so
-// every K/V fragment read from LDS feeds two MFMAs.
+// Four waves per workgroup; each wave owns QB blocks of 32 query rows.  The
+// code is written for any QB, but QB = 1: two blocks per wave (one wave per
+// SIMD with up to 512 registers, each K/V fragment feeding two MFMAs) made
+// the register allocator spill heavily.
 template <int D>
 struct FwdTile {
   static constexpr int QB = 1;
