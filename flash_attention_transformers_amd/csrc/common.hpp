@@ -8,16 +8,15 @@
 // A C tile can feed the next MFMA as its B operand directly (lane keeps its
 // column): register i = 8t + e of the C tile becomes k-slot 8g + e of k-step
 // t.  The row it carries is 16t + swz(8g + e), where swz swaps bits 2 and 3
-// of a 4-bit index.  The other operand of that MFMA (read from LDS) is
-// therefore stored with its contraction index permuted by swz inside every
-// aligned group of 16; since a contraction is a sum, the order is free.
+// of a 4-bit index.  The other operand of that MFMA is therefore read from
+// LDS in the same permuted order (ld_trans_operand below); since a
+// contraction is a sum, the order is free.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -29,11 +28,6 @@ namespace mattn {
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Swap bits 2 and 3 of the low nibble: position <-> row inside a group of 16.
-__host__ __device__ __forceinline__ constexpr int swz(int x) {
-  return (x & ~12) | ((x & 4) << 1) | ((x & 8) >> 1);
 }
 
 // Row of the C tile held by register i of lane group g.
@@ -90,13 +84,6 @@ __device__ __forceinline__ bf16x8 ld_trans_operand(const bf16* tile, int pitch, 
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-__device__ __forceinline__ bf16x8 zero_bf16x8() {
-  bf16x8 z;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) z[e] = (bf16)0.0f;
-  return z;
-}
 
 __device__ __forceinline__ f32x16 zero_f32x16() {
   f32x16 z;
@@ -174,33 +161,8 @@ struct DirectTile {
   }
 };
 
-// 16-byte global load of 8 bf16, or zeros when !valid.
-__device__ __forceinline__ uint4 ld16(const bf16* p, bool valid) {
-  if (valid) return *reinterpret_cast<const uint4*>(p);
-  return make_uint4(0, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t ld4(const bf16* p, bool valid) {
-  if (valid) return *reinterpret_cast<const uint32_t*>(p);
-  return 0u;
-}
-
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
   return __builtin_bit_cast(bf16x8, u);
-}
-
-// Eight bf16 pairs (d, d+1) of eight rows -> column d and column d+1 as two
-// 8-element vectors (low halves and high halves).
-__device__ __forceinline__ void split_pairs(const uint32_t (&w)[8], uint4& lo, uint4& hi) {
-  uint32_t l[4], h[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t a = w[2 * e], b = w[2 * e + 1];
-    l[e] = __builtin_amdgcn_perm(b, a, 0x05040100u);  // (b.lo << 16) | a.lo
-    h[e] = __builtin_amdgcn_perm(b, a, 0x07060302u);  // (b.hi << 16) | a.hi
-  }
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
