@@ -32,8 +32,9 @@
 //        S^T = K Q^T, dP^T = V dO^T        (lane = query column)
 //        dQ^T += K^T dS^T
 //     and the two key-half partials are summed in a fixed order at the end.
-// Q/dO and K/V tiles are staged row-major in LDS, once each; every
-// transposed MFMA operand (dO^T, Q^T, K^T) is read from that copy with
+// Q/dO and K/V tiles are staged in LDS once each, in a layout (SwzTile)
+// whose row reads and transposed reads are both free of bank conflicts;
+// every transposed MFMA operand (dO^T, Q^T, K^T) is read from that copy with
 // ds_read_b64_tr_b16.
 #include <type_traits>
 
@@ -97,13 +98,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      int nsplit, int q_chunk) {
   constexpr int BMQ = BWD_BMQ;            // query rows per step (two 32-row sub-blocks)
   constexpr int NSUB = BMQ / 32;
-  constexpr int RP = RowPitch<D>::value;
+  using SW = SwzTile<D>;
+  constexpr int SP = SW::P;
   constexpr int CH = BMQ * D / 8 / DKDV_THREADS;  // 16-byte chunks per thread per tensor
   static_assert(CH >= 1 && (BMQ * D / 8) % DKDV_THREADS == 0, "tile loader must tile the workgroup");
-  // Q and dO tiles at the row-operand pitch, double-buffered: step t reads
-  // tiles t and t+1.  The transposed reads (dO^T, Q^T) use the same copy.
-  __shared__ __attribute__((aligned(16))) bf16 Qs[DKDV_NBUF][BMQ * RP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[DKDV_NBUF][BMQ * RP];
+  // Q and dO tiles in the swizzled layout, double-buffered: step t reads
+  // tiles t and t+1.  Row and transposed reads (dO^T, Q^T) use the same copy.
+  __shared__ __attribute__((aligned(16))) bf16 Qs[DKDV_NBUF][BMQ * SP];
+  __shared__ __attribute__((aligned(16))) bf16 dOs[DKDV_NBUF][BMQ * SP];
   // P handed from each P-wave to its dS-wave: [slice][sub-block][blk][lane][4].
   __shared__ __attribute__((aligned(16))) float Pex[4 * NSUB * 4 * 64 * 4];
   __shared__ __attribute__((aligned(16))) float lse_s[DKDV_NBUF][BMQ];
@@ -182,9 +184,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
     for (int r2 = 0; r2 < CH; ++r2) {
       const int ch = tid + DKDV_THREADS * r2;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Qs[buf][row * RP + col]) = qreg[r2];
-      *reinterpret_cast<uint4*>(&dOs[buf][row * RP + col]) = doreg[r2];
+      const int off = SW::store_off(ch / (D / 8), ch % (D / 8));
+      *reinterpret_cast<uint4*>(&Qs[buf][off]) = qreg[r2];
+      *reinterpret_cast<uint4*>(&dOs[buf][off]) = doreg[r2];
     }
     if (tid < BMQ) {
       // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
@@ -195,6 +197,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   };
 
   float* pex = Pex + slice * (NSUB * 4 * 64 * 4);
+  SW sw;
+  sw.init(lane);
   // S = Q K^T (P-wave) or dP = dO V^T (dS-wave) for one tile: lane = key
   // column, registers = query rows; both sub-blocks as independent chains.
   auto score_tile = [&](const bf16* tile, f32x16 (&sc)[NSUB]) {
@@ -204,7 +208,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int st = 0; st < D / 16; ++st)
 #pragma unroll
       for (int qb = 0; qb < NSUB; ++qb)
-        sc[qb] = mfma32(ld_row_operand(tile, RP, qb * 32, 16 * st, lane), kvf[st], sc[qb]);
+        sc[qb] = mfma32(sw.row(tile, qb * 32, st), kvf[st], sc[qb]);
   };
   // P = 2^(S*c - LSE*log2e), masked above the causal diagonal; P goes to
   // the dS-wave through LDS and stays in registers as bf16 for dV.
@@ -241,7 +245,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         bf16x8 a[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          a[db] = ld_trans_operand(dOs[buf], RP, qb * 32 + 16 * t, db * 32, lane);
+          a[db] = sw.trans(dOs[buf], qb * 32 + 16 * t, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[qb][t], acc[db]);
       }
@@ -269,7 +273,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         bf16x8 a[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          a[db] = ld_trans_operand(Qs[buf], RP, qb * 32 + 16 * t, db * 32, lane);
+          a[db] = sw.trans(Qs[buf], qb * 32 + 16 * t, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], dsb[qb][t], acc[db]);
       }
@@ -408,17 +412,18 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const float* __restrict__ LSE, const float* __restrict__ DLT,
                    bf16* __restrict__ dQ, int Hq, int G, int Sq, int Skv, float scale, float c,
                    int n_qt) {
-  constexpr int RP = RowPitch<D>::value;
+  using SW = SwzTile<D>;
+  constexpr int SP = SW::P;
   constexpr int CH = DQ_BN * D / 8 / DQ_THREADS;  // 16-byte chunks per thread per tensor
   static_assert(CH >= 1 && (DQ_BN * D / 8) % DQ_THREADS == 0, "tile loader must tile the workgroup");
-  // K and V tiles at the row-operand pitch during the walk (K^T is read
+  // K and V tiles in the swizzled layout during the walk (K^T is read
   // transposed from the same K copy); afterwards the same LDS holds the
   // key-half partials of dQ^T: [slice][db][r][lane][4] floats.
-  constexpr int TILE_BYTES = DQ_BN * 2 * RP * 2;
+  constexpr int TILE_BYTES = DQ_BN * 2 * SP * 2;
   constexpr int RED_BYTES = 4 * (D / 32) * 4 * 64 * 4 * 4;
   __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES];
   bf16* Ks = reinterpret_cast<bf16*>(smem);
-  bf16* Vs = Ks + DQ_BN * RP;
+  bf16* Vs = Ks + DQ_BN * SP;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -433,6 +438,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int qw0 = q0 + slice * 32;
   const int qrow = qw0 + l32;
   const int diag = Skv - Sq;
+  SW sw;
+  sw.init(lane);
 
   const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
   const Buf dobuf(dO + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
@@ -474,9 +481,9 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
     for (int r = 0; r < CH; ++r) {
       const int ch = tid + DQ_THREADS * r;
-      const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Ks[row * RP + col]) = kreg[r];
-      *reinterpret_cast<uint4*>(&Vs[row * RP + col]) = vreg[r];
+      const int off = SW::store_off(ch / (D / 8), ch % (D / 8));
+      *reinterpret_cast<uint4*>(&Ks[off]) = kreg[r];
+      *reinterpret_cast<uint4*>(&Vs[off]) = vreg[r];
     }
     __syncthreads();
     if (kt + 1 < n_kt) load_tile(j0 + DQ_BN);
@@ -490,8 +497,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         bf16x8 ak[4], av[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          ak[u] = ld_row_operand(Ks, RP, kb0, 16 * (st0 + u), lane);
-          av[u] = ld_row_operand(Vs, RP, kb0, 16 * (st0 + u), lane);
+          ak[u] = sw.row(Ks, kb0, st0 + u);
+          av[u] = sw.row(Vs, kb0, st0 + u);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -515,7 +522,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         bf16x8 a[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          a[db] = ld_trans_operand(Ks, RP, kb0 + 16 * t, db * 32, lane);
+          a[db] = sw.trans(Ks, kb0 + 16 * t, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) adq[db] = mfma32(a[db], dsb[t], adq[db]);
       }

@@ -45,9 +45,8 @@ __device__ __forceinline__ constexpr int crow(int i, int g) {
 //     disjoint 64-byte bank segments.
 // No single pitch serves both.  Measured on MI355X: 197 (rows, 304 B) and 182
 // (transposed, 320 B) bytes per clock per CU, against 62 and 116 with the
-// pitches swapped.  A tile that is read both ways is still stored once, at
-// the row pitch: a second copy cost more LDS write traffic than the slower
-// transposed reads lose.
+// pitches swapped.  A tile that is read both ways is stored once, in the
+// swizzled layout of SwzTile below.
 template <int D>
 struct RowPitch {
   static constexpr int value = D == 128 ? 152 : 104;
@@ -82,6 +81,51 @@ __device__ __forceinline__ bf16x8 ld_trans_operand(const bf16* tile, int pitch, 
   const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * pitch));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
+// Layout of a [rows x D] bf16 tile in LDS that is read both as row operands
+// and transposed: pitch TrPitch<D>, and the 16-byte chunk c of row r held at
+// chunk position c ^ ((r >> 2) & 3).  At that pitch the four rows of a
+// transposed read already fall in disjoint 64-byte bank segments, and the XOR
+// (which only permutes chunks inside aligned 64-byte blocks) leaves that
+// intact, while it moves the sixteen rows of a row read, which the pitch
+// alone maps onto four segments, onto sixteen distinct 16-byte bank groups.
+// Because the XOR touches only the low two bits of the chunk index, a lane's
+// address for any k-step or d-block is one of two per-lane bases plus a
+// compile-time offset.  Reads start at rows that are multiples of 16.
+template <int D>
+struct SwzTile {
+  static constexpr int P = TrPitch<D>::value;
+  int rbase[2];  // row operand, k-step parity b: row l32, chunk (2b + g) ^ F(l32)
+  int tbase[2];  // transposed operand, rows 0..7 (h = 0) and 8..15 (h = 1) of a 16-row step
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) rbase[b] = l32 * P + 8 * ((2 * b + g) ^ ((l32 >> 2) & 3));
+    const int j = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 4 * (j >> 1) + (s >> 2) + 8 * h;
+      tbase[h] = r * P + 8 * ((2 * (j & 1) + ((s >> 1) & 1)) ^ ((r >> 2) & 3)) + 4 * (s & 1);
+    }
+  }
+  // Element offset of the chunk that holds columns 8*chunk .. 8*chunk+7 of row `row`.
+  static __device__ __forceinline__ int store_off(int row, int chunk) {
+    return row * P + 8 * (chunk ^ ((row >> 2) & 3));
+  }
+  // ld_row_operand of this layout: rows row0 .. row0+31, columns 16st .. 16st+15.
+  __device__ __forceinline__ bf16x8 row(const bf16* tile, int row0, int st) const {
+    return *reinterpret_cast<const bf16x8*>(tile + row0 * P + 32 * (st >> 1) + rbase[st & 1]);
+  }
+  // ld_trans_operand of this layout: operand rows = tile columns 32db .. 32db+31,
+  // k-slots = tile rows row0 + swz(8g + e), as there.
+  __device__ __forceinline__ bf16x8 trans(const bf16* tile, int row0, int db) const {
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    const bf16* p = tile + row0 * P + 32 * db;
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tbase[0]));
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tbase[1]));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
