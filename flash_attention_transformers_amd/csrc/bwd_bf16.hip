@@ -400,35 +400,78 @@ void bwd_reduce_kernel(const float* __restrict__ part, bf16* __restrict__ dK,
 
 // ----------------------------------------------------------------------------
 // 3. dQ
-constexpr int DQ_BM = 128;
-constexpr int DQ_BN = 64;
+constexpr int DQ_SLICES = 2;               // 32-row query slices per workgroup
+constexpr int DQ_BM = 32 * DQ_SLICES;      // query rows per workgroup
+constexpr int DQ_BN = 64;                  // keys per tile
+constexpr int DQ_THREADS = 128 * DQ_SLICES;  // DQ_SLICES query slices x 2 key halves
 
-constexpr int DQ_THREADS = 512;  // 4 query slices x 2 key halves
+// Direct global -> LDS copy of one K tile and one V tile (DQ_BN rows each)
+// into one buffer laid out as [K tile | V tile], both in the SwzTile layout.
+// The swizzle only permutes 16-byte chunks within a row, so it is applied on
+// the global side: LDS slot (row, position) receives global chunk
+// position ^ ((row >> 2) & 3), and every wave writes 64 consecutive slots.
+// The two tiles together are a whole number of rounds of the workgroup's
+// threads, so every wave issues the same number of copies per buffer.
+template <int D>
+struct DqKvCopy {
+  static constexpr int P = SwzTile<D>::P;
+  static constexpr int SLOTS_PER_ROW = P / 8;
+  static constexpr int TILE_SLOTS = DQ_BN * SLOTS_PER_ROW;  // per tensor
+  static constexpr int ROUNDS = 2 * TILE_SLOTS / DQ_THREADS;
+  static constexpr int BUF_ELEMS = 2 * TILE_SLOTS * 8;
+  static_assert(2 * TILE_SLOTS % DQ_THREADS == 0 && TILE_SLOTS % 64 == 0, "whole rounds");
+  uint32_t off[ROUNDS];
+  int w0;  // first slot of this wave in round 0 (scalar)
+  __device__ __forceinline__ void init(int tid) {
+    w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int q = r * DQ_THREADS + tid;
+      const int qq = q % TILE_SLOTS;  // slot within its tensor's tile
+      const int row = qq / SLOTS_PER_ROW, pos = qq - row * SLOTS_PER_ROW;
+      const int ch = pos ^ ((row >> 2) & 3);
+      off[r] = pos < D / 8 ? (uint32_t)(row * D + ch * 8) * 2 : 0x80000000u;
+    }
+  }
+  // Tile rows start at the descriptors' bases; rows past their ends load zeros.
+  __device__ __forceinline__ void load(const Buf& k, const Buf& v, bf16* buf) const {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int q0 = r * DQ_THREADS + w0;
+      ld16_to_lds(q0 < TILE_SLOTS ? k : v, off[r], buf + q0 * 8);
+    }
+  }
+};
 
+// dQ_i = scale * sum_j dS_ij K_j for a block of DQ_BM query rows.  Each wave
+// keeps its 32 rows of Q and dO in registers and takes one 32-key half of
+// every 64-key tile.  K/V tiles arrive by direct copies into two LDS
+// buffers, one tile ahead, with one barrier per tile.  Each buffer is its own
+// LDS object, so reads of the current tile never wait for the copies in
+// flight to the other.  Small workgroups let two of them share a CU: the two
+// waves on a SIMD then belong to different workgroups and drift out of phase,
+// so the VALU work of one (dS) overlaps the MFMA work of the other.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(DQ_THREADS)
+__global__ __launch_bounds__(DQ_THREADS, 2)
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ V, const bf16* __restrict__ dO,
                    const float* __restrict__ LSE, const float* __restrict__ DLT,
                    bf16* __restrict__ dQ, int Hq, int G, int Sq, int Skv, float scale, float c,
                    int n_qt) {
   using SW = SwzTile<D>;
-  constexpr int SP = SW::P;
-  constexpr int CH = DQ_BN * D / 8 / DQ_THREADS;  // 16-byte chunks per thread per tensor
-  static_assert(CH >= 1 && (DQ_BN * D / 8) % DQ_THREADS == 0, "tile loader must tile the workgroup");
-  // K and V tiles in the swizzled layout during the walk (K^T is read
-  // transposed from the same K copy); afterwards the same LDS holds the
-  // key-half partials of dQ^T: [slice][db][r][lane][4] floats.
-  constexpr int TILE_BYTES = DQ_BN * 2 * SP * 2;
-  constexpr int RED_BYTES = 4 * (D / 32) * 4 * 64 * 4 * 4;
-  __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES];
-  bf16* Ks = reinterpret_cast<bf16*>(smem);
-  bf16* Vs = Ks + DQ_BN * SP;
+  using Copy = DqKvCopy<D>;
+  constexpr int VOFF = Copy::TILE_SLOTS * 8;  // V tile's offset in a buffer (elements)
+  __shared__ __attribute__((aligned(16))) bf16 KV0[Copy::BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 KV1[Copy::BUF_ELEMS];
+  auto KVbuf = [&](auto b) __attribute__((always_inline)) -> bf16* {
+    if constexpr (decltype(b)::value == 0) return KV0; else return KV1;
+  };
+  static_assert(SW::P * DQ_BN == VOFF, "V tile follows the K tile");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int slice = wave & 3;   // 32 query rows
-  const int kh = wave >> 2;     // which 32-key half of every tile this wave takes
+  const int slice = wave % DQ_SLICES;  // 32 query rows
+  const int kh = wave / DQ_SLICES;     // which 32-key half of every tile this wave takes
   int bh, qt;
   tile_of_block(blockIdx.x, gridDim.x / n_qt, n_qt, CAUSAL, bh, qt);
   const int h = bh % Hq, b = bh / Hq;
@@ -441,10 +484,25 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   SW sw;
   sw.init(lane);
 
+  int kv_end = Skv;
+  if (CAUSAL) kv_end = min(Skv, q0 + DQ_BM + diag);
+  const int n_kt = (kv_end + DQ_BN - 1) / DQ_BN;
+
+  Copy cp;
+  cp.init(tid);
+  const bf16* Kh = K + kv_off;
+  const bf16* Vh = V + kv_off;
+  auto issue = [&](int kt, bf16* dst) __attribute__((always_inline)) {
+    const int j0 = kt * DQ_BN;
+    const uint32_t nb = (uint32_t)(Skv - j0) * D * 2;
+    cp.load(Buf(Kh + (size_t)j0 * D, nb), Buf(Vh + (size_t)j0 * D, nb), dst);
+  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  if (n_kt > 0) issue(0, KV0);
+
   const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
   const Buf dobuf(dO + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
-  const Buf kbuf(K + kv_off, (uint32_t)Skv * D * 2);
-  const Buf vbuf(V + kv_off, (uint32_t)Skv * D * 2);
   bf16x8 qf[D / 16], dof[D / 16];
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
@@ -455,41 +513,22 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const float lse2 = qrow < Sq ? LSE[(size_t)bh * Sq + qrow] * MATTN_LOG2E : MATTN_INF;
   const float dl = qrow < Sq ? DLT[(size_t)bh * Sq + qrow] : 0.f;
 
-  int kv_end = Skv;
-  if (CAUSAL) kv_end = min(Skv, q0 + DQ_BM + diag);
-  const int n_kt = (kv_end + DQ_BN - 1) / DQ_BN;
-
-  uint4 kreg[CH], vreg[CH];
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      const int ch = tid + DQ_THREADS * r;
-      const uint32_t off = (uint32_t)((j0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2;
-      kreg[r] = kbuf.ld16(off);
-      vreg[r] = vbuf.ld16(off);
-    }
-  };
-
   f32x16 adq[D / 32];  // partial dQ^T over this wave's key halves
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adq[db] = zero_f32x16();
 
-  if (n_kt > 0) load_tile(0);
-  for (int kt = 0; kt < n_kt; ++kt) {
+  const int kb0 = kh * 32;  // this wave's 32 keys of the tile
+  // Tile kt sits in buffer kt & 1.  At its top this thread's copies of tile
+  // kt have landed; the barrier makes that true for everyone and ends every
+  // read of tile kt-1, whose buffer then takes tile kt+1.
+  auto tile = [&](auto bsel, int kt) __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    barrier_keep_copies();
+    if (kt + 1 < n_kt) issue(kt + 1, KVbuf(std::integral_constant<int, decltype(bsel)::value ^ 1>{}));
+    const bf16* Ks = KVbuf(bsel);
+    const bf16* Vs = Ks + VOFF;
     const int j0 = kt * DQ_BN;
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      const int ch = tid + DQ_THREADS * r;
-      const int off = SW::store_off(ch / (D / 8), ch % (D / 8));
-      *reinterpret_cast<uint4*>(&Ks[off]) = kreg[r];
-      *reinterpret_cast<uint4*>(&Vs[off]) = vreg[r];
-    }
-    __syncthreads();
-    if (kt + 1 < n_kt) load_tile(j0 + DQ_BN);
-
-    const int kb0 = kh * 32;  // this wave's 32 keys of the tile
-    auto step = [&](auto masked) {
+    auto step = [&](auto masked) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(masked)::value;
       f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
@@ -521,8 +560,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int t = 0; t < 2; ++t) {
         bf16x8 a[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          a[db] = sw.trans(Ks, kb0 + 16 * t, db);
+        for (int db = 0; db < D / 32; ++db) a[db] = sw.trans(Ks, kb0 + 16 * t, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) adq[db] = mfma32(a[db], dsb[t], adq[db]);
       }
@@ -532,12 +570,20 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       step(std::true_type{});
     else
       step(std::false_type{});
+  };
+  int kt = 0;
+  for (; kt + 2 <= n_kt; kt += 2) {
+    tile(B0{}, kt);
+    tile(B1{}, kt + 1);
   }
+  if (kt < n_kt) tile(B0{}, kt);
 
   // Sum the two key-half partials in a fixed order (half 0 + half 1) through
-  // LDS, reusing the K tile buffer, and write dQ.
+  // LDS, reusing the first tile buffer, and write dQ.
+  constexpr int RED_FLOATS = (D / 32) * 16 * 64;  // per slice
+  static_assert(DQ_SLICES * RED_FLOATS * 4 <= Copy::BUF_ELEMS * 2, "partials fit in one buffer");
   __syncthreads();
-  float* red_slice = reinterpret_cast<float*>(smem) + slice * (D / 32) * 16 * 64;
+  float* red_slice = reinterpret_cast<float*>(KV0) + slice * RED_FLOATS;
   if (kh == 1) {
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)

@@ -72,15 +72,48 @@ __device__ __forceinline__ bf16x8 ld_row_operand(const bf16* tile, int pitch, in
 // reads tile row row0 + 8h + 4(j/2) + s/4 at columns col0 + 16(j%2) + 4(s%4)
 // .. +3.  `pitch` must be a multiple of 4.
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+
+// One ds_read_b64_tr_b16.  The compiler tracks direct global->LDS copies in
+// flight per LDS object (the alias scopes it gives each __shared__ variable),
+// so a read of one buffer only waits for copies into that same buffer; a
+// kernel that keeps its double buffers in separate __shared__ variables can
+// read one while copies into the other are still in flight.
+__device__ __forceinline__ bf16x4_t ds_read_tr(const lds_bf16x4* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(const_cast<lds_bf16x4*>(p));
+}
+
 __device__ __forceinline__ bf16x8 ld_trans_operand(const bf16* tile, int pitch, int row0,
                                                    int col0, int lane) {
   const int j = lane >> 4, s = lane & 15;
   const bf16* p = tile + (row0 + 4 * (j >> 1) + (s >> 2)) * pitch + col0 + 16 * (j & 1) + 4 * (s & 3);
-  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
-  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + 8 * pitch));
+  const bf16x4_t lo = ds_read_tr((const lds_bf16x4*)(p));
+  const bf16x4_t hi = ds_read_tr((const lds_bf16x4*)(p + 8 * pitch));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+
+// ld_trans_operand with the lane-dependent part of the address computed once.
+// The compiler attaches an LDS object's alias scope only to accesses whose
+// address it can trace back to that object through a few address steps; an
+// address built from several separately combined lane terms can lose it, and
+// the read then waits for every direct copy in flight.  Here the lane term is
+// one opaque value, so each read's address is the tile base + that value + a
+// compile-time constant.
+struct TransReader {
+  int off;  // element offset of this lane's first chunk for row0 = col0 = 0
+  __device__ __forceinline__ void init(int pitch, int lane) {
+    const int j = lane >> 4, s = lane & 15;
+    off = (4 * (j >> 1) + (s >> 2)) * pitch + 16 * (j & 1) + 4 * (s & 3);
+    asm volatile("" : "+v"(off));
+  }
+  __device__ __forceinline__ bf16x8 operator()(const bf16* tile, int pitch, int row0,
+                                               int col0) const {
+    const bf16* p = tile + off;
+    const bf16x4_t lo = ds_read_tr((const lds_bf16x4*)(p + row0 * pitch + col0));
+    const bf16x4_t hi = ds_read_tr((const lds_bf16x4*)(p + (row0 + 8) * pitch + col0));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
 
 // Layout of a [rows x D] bf16 tile in LDS that is read both as row operands
 // and transposed: pitch TrPitch<D>, and the 16-byte chunk c of row r held at
@@ -107,6 +140,9 @@ struct SwzTile {
       const int r = 4 * (j >> 1) + (s >> 2) + 8 * h;
       tbase[h] = r * P + 8 * ((2 * (j & 1) + ((s >> 1) & 1)) ^ ((r >> 2) & 3)) + 4 * (s & 1);
     }
+    // Opaque to the optimizer, so that every read's address stays the tile
+    // base + one lane value + a constant (see TransReader).
+    asm volatile("" : "+v"(rbase[0]), "+v"(rbase[1]), "+v"(tbase[0]), "+v"(tbase[1]));
   }
   // Element offset of the chunk that holds columns 8*chunk .. 8*chunk+7 of row `row`.
   static __device__ __forceinline__ int store_off(int row, int chunk) {
@@ -119,10 +155,9 @@ struct SwzTile {
   // ld_trans_operand of this layout: operand rows = tile columns 32db .. 32db+31,
   // k-slots = tile rows row0 + swz(8g + e), as there.
   __device__ __forceinline__ bf16x8 trans(const bf16* tile, int row0, int db) const {
-    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
     const bf16* p = tile + row0 * P + 32 * db;
-    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tbase[0]));
-    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p + tbase[1]));
+    const bf16x4_t lo = ds_read_tr((const lds_bf16x4*)(p + tbase[0]));
+    const bf16x4_t hi = ds_read_tr((const lds_bf16x4*)(p + tbase[1]));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
@@ -160,6 +195,19 @@ struct Buf {
   }
 };
 
+// Workgroup barrier for loops whose LDS traffic between barriers is reads
+// plus direct copies that each wave has already waited for (s_waitcnt
+// vmcnt).  __syncthreads() adds a release fence, which waits for every
+// outstanding vector memory operation, including direct copies issued for
+// later tiles; this barrier leaves those in flight.  The empty asm statements
+// keep the compiler from moving memory accesses across it.  Not for use after
+// ds_write: those need the fence (or an explicit lgkmcnt wait) first.
+__device__ __forceinline__ void barrier_keep_copies() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane L's bytes land at
 // lds_base + 16 L (lds_base wave-uniform).  Offsets outside the descriptor's
 // range write zeros.  Completion is tracked by vmcnt, like other vector
@@ -181,24 +229,28 @@ struct DirectTile {
   static constexpr int SLOTS_PER_ROW = PITCH / 8;
   static constexpr int SLOTS = ROWS * SLOTS_PER_ROW;
   static constexpr int ROUNDS = (SLOTS + NT - 1) / NT;
+  // LDS elements to allocate: whole waves of slots, so a wave that straddles
+  // the tile's end writes its surplus slots (as zeros) into padding.
+  static constexpr int LDS_ELEMS = (SLOTS + 63) / 64 * 64 * 8;
   static_assert(PITCH % 8 == 0 && PITCH >= D, "pitch");
   uint32_t off[ROUNDS];
+  int w0;  // first slot of this wave in round 0; wave-uniform, kept in a scalar register
   __device__ __forceinline__ void init(int tid) {
+    w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
       const int q = r * NT + tid;
       const int row = q / SLOTS_PER_ROW, c = q - row * SLOTS_PER_ROW;
-      off[r] = (c < D / 8) ? (uint32_t)(row * D + c * 8) * 2 : 0x80000000u;
+      off[r] = (q < SLOTS && c < D / 8) ? (uint32_t)(row * D + c * 8) * 2 : 0x80000000u;
     }
   }
   // Copy rows [0, ROWS) of `src` (a descriptor whose base is the tile's first
-  // row) into `lds` (the tile, PITCH-padded).  Slots past the tile's end are
-  // skipped (a whole wave at a time, since SLOTS is a multiple of 64).
+  // row) into `lds` (the tile, PITCH-padded, LDS_ELEMS long).  Waves whose
+  // slots all lie past the tile's end skip the round.
   __device__ __forceinline__ void load(const Buf& src, bf16* lds, int tid) const {
-    static_assert(SLOTS % 64 == 0, "partial rounds must end on a wave boundary");
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
-      const int q0 = r * NT + (tid & ~63);  // first slot of this wave in round r
+      const int q0 = r * NT + w0;  // first slot of this wave in round r
       if (SLOTS % NT == 0 || q0 < SLOTS)
         ld16_to_lds(src, off[r], lds + q0 * 8);
     }

@@ -25,14 +25,14 @@
 //    softmax arithmetic issues between matrix instructions instead of
 //    after them.
 // Softmax runs in the log2 domain: t = s * scale * log2(e), p = 2^(t - m).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace mattn {
 
 namespace {
-
-constexpr int FWD_BN = 64;
 
 // Four waves per workgroup; each wave owns QB blocks of 32 query rows.  The
 // code is written for any QB, but QB = 1: two blocks per wave (one wave per
@@ -41,13 +41,15 @@ constexpr int FWD_BN = 64;
 template <int D>
 struct FwdTile {
   static constexpr int QB = 1;
+  static constexpr int BN = 64;       // keys per tile
+  static constexpr int KB = BN / 32;  // 32-key blocks per tile
   static constexpr int WAVES = 4;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int BM = 32 * QB * WAVES;     // query rows per workgroup
   static constexpr int KP = RowPitch<D>::value;  // K tile: read as row operands
   static constexpr int VP = TrPitch<D>::value;   // V tile: read transposed
-  using KTile = DirectTile<D, FWD_BN, KP, THREADS>;
-  using VTile = DirectTile<D, FWD_BN, VP, THREADS>;
+  using KTile = DirectTile<D, BN, KP, THREADS>;
+  using VTile = DirectTile<D, BN, VP, THREADS>;
 };
 
 template <int D, bool CAUSAL>
@@ -57,10 +59,22 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      float* __restrict__ LSE, int Hq, int G, int Sq, int Skv,
                      float c /* scale*log2(e) */, int n_qt) {
   using T = FwdTile<D>;
-  constexpr int QB = T::QB;
-  // Double-buffered K and V tiles, filled straight from global memory.
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][FWD_BN * T::KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][FWD_BN * T::VP];
+  constexpr int QB = T::QB, KB = T::KB, FWD_BN = T::BN;
+  // Double-buffered K and V tiles, filled straight from global memory.  Each
+  // buffer is its own LDS object: the compiler tracks copies in flight per
+  // object, so reading one buffer does not wait for copies into another.
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[T::KTile::LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[T::KTile::LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[T::VTile::LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[T::VTile::LDS_ELEMS];
+  auto Ks = [&](auto parity) -> bf16* {
+    if constexpr (decltype(parity)::value == 0) return Ks0; else return Ks1;
+  };
+  auto Vs = [&](auto parity) -> bf16* {
+    if constexpr (decltype(parity)::value == 0) return Vs0; else return Vs1;
+  };
+  using Even = std::integral_constant<int, 0>;
+  using Odd = std::integral_constant<int, 1>;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -113,13 +127,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   vt_ld.init(tid);
   // Tile t's descriptors start at its first row and end at Skv, so rows past
   // the end (and pad slots) read as zeros.
-  auto issue_k = [&](int t) {
+  // Tile t goes to buffer t & 1; callers pass that parity as a compile-time
+  // constant, so that every LDS address names its buffer statically and the
+  // compiler can see that reads of one buffer do not depend on copies still
+  // in flight to the other.
+  auto issue_k = [&](int t, bf16* dst) {
     const int j0 = t * FWD_BN;
-    kt_ld.load(Buf(Kh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), Ks[t & 1], tid);
+    kt_ld.load(Buf(Kh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), dst, tid);
   };
-  auto issue_v = [&](int t) {
+  auto issue_v = [&](int t, bf16* dst) {
     const int j0 = t * FWD_BN;
-    vt_ld.load(Buf(Vh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), Vs[t & 1], tid);
+    vt_ld.load(Buf(Vh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), dst, tid);
   };
   // Whether some key of tile t is invisible to some query of this wave.
   auto tile_masked = [&](int t) {
@@ -142,19 +160,19 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   float m[QB], l[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) { m[qb] = -MATTN_INF; l[qb] = 0.f; }
-  bf16x8 pb[QB][2][2];  // P^T of the current tile, B operands of O^T += V^T P^T
+  bf16x8 pb[QB][KB][2];  // P^T of the current tile, B operands of O^T += V^T P^T
 
   // S^T = K Q^T for one 64-key tile: per query block, two 32-key blocks
   // (lane = query column, registers = keys); each K fragment feeds QB MFMAs.
-  auto s_tile = [&](const bf16* Kb, f32x16 (&sc)[QB][2]) {
+  auto s_tile = [&](const bf16* Kb, f32x16 (&sc)[QB][KB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) sc[qb][kb] = zero_f32x16();
+      for (int kb = 0; kb < KB; ++kb) sc[qb][kb] = zero_f32x16();
 #pragma unroll
     for (int st = 0; st < D / 16; ++st)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const bf16x8 a = ld_row_operand(Kb, T::KP, kb * 32, 16 * st, lane);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = mfma32(a, qf[qb][st], sc[qb][kb]);
@@ -162,18 +180,18 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   };
   // Row max of a tile's raw scores; the masked form first overwrites
   // invisible keys (past Skv, or above the causal diagonal) with -inf.
-  auto max_plain = [&](const f32x16 (&sc)[2]) {
+  auto max_plain = [&](const f32x16 (&sc)[KB]) {
     float mx = sc[0][0];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb][i]);
     return mx;
   };
-  auto max_masked = [&](f32x16 (&sc)[2], int t, int qrow) {
+  auto max_masked = [&](f32x16 (&sc)[KB], int t, int qrow) {
     float mx = -MATTN_INF;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = t * FWD_BN + kb * 32 + crow(i, g);
@@ -212,15 +230,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
   };
   // O^T += V^T P^T; each V^T fragment feeds QB MFMAs.
+  TransReader vtr;
+  vtr.init(T::VP, lane);
   auto pv_tile = [&](const bf16* Vb) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         bf16x8 a[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          a[db] = ld_trans_operand(Vb, T::VP, kb * 32 + 16 * t, db * 32, lane);
+          a[db] = vtr(Vb, T::VP, kb * 32 + 16 * t, db * 32);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -235,12 +255,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // then moves the reference max for tile t+1.  K runs one tile ahead of V:
   // step t reads K(t+1) and V(t) and loads K(t+2) and V(t+1) behind them,
   // one barrier per step.
-  constexpr int NMF = 16 * QB;  // MFMAs per phase
-  auto step = [&](int t, f32x16 (&cur)[QB][2], f32x16 (&nxt)[QB][2]) {
+  constexpr int NMF = QB * KB * (D / 16);  // MFMAs per phase
+  auto step = [&](auto p0, int t, f32x16 (&cur)[QB][KB], f32x16 (&nxt)[QB][KB]) {
+    // p0 = t & 1, p1 = the other buffer
+    const std::integral_constant<int, decltype(p0)::value ^ 1> p1;
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this thread's copies landed
     __syncthreads();                     // everyone's, and step t-1 is done everywhere
-    if (t + 2 < n_kt) issue_k(t + 2);
-    issue_v(t + 1);
+    if (t + 2 < n_kt) issue_k(t + 2, Ks(p0));
+    issue_v(t + 1, Vs(p1));
     float rs[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -248,11 +270,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
     // Phase 1: the MFMAs of S(t+1) with the 112 VALU instructions per query
     // block that turn S(t) into P(t).
-    s_tile(Ks[(t + 1) & 1], nxt);
+    s_tile(Ks(p1), nxt);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) exp_block(cur[qb][kb], qb, kb, rs[qb]);
+      for (int kb = 0; kb < KB; ++kb) exp_block(cur[qb][kb], qb, kb, rs[qb]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
@@ -272,7 +294,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     // Phase 2: the MFMAs of O += P(t) V(t) with the row max of S(t+1).
     float mx[QB];
     if (tile_masked(t + 1)) {
-      pv_tile(Vs[t & 1]);
+      pv_tile(Vs(p0));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = max_masked(nxt[qb], t + 1, qrow_of(qb));
 #pragma unroll
@@ -284,7 +306,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
     } else {
-      pv_tile(Vs[t & 1]);
+      pv_tile(Vs(p0));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = max_plain(nxt[qb]);
 #pragma unroll
@@ -299,26 +321,26 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) update_ref(qb, mx[qb]);
   };
-  auto last_step = [&](int t, f32x16 (&cur)[QB][2]) {
+  auto last_step = [&](auto p0, f32x16 (&cur)[QB][KB]) {
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float rs[4] = {0.f, 0.f, 0.f, 0.f};
-      exp_block(cur[qb][0], qb, 0, rs);
-      exp_block(cur[qb][1], qb, 1, rs);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) exp_block(cur[qb][kb], qb, kb, rs);
       l[qb] += (rs[0] + rs[1]) + (rs[2] + rs[3]);
     }
-    pv_tile(Vs[t & 1]);
+    pv_tile(Vs(p0));
   };
 
-  f32x16 sa[QB][2], sb[QB][2];
-  issue_k(0);
-  if (n_kt > 1) issue_k(1);
-  issue_v(0);
+  f32x16 sa[QB][KB], sb[QB][KB];
+  issue_k(0, Ks(Even{}));
+  if (n_kt > 1) issue_k(1, Ks(Odd{}));
+  issue_v(0, Vs(Even{}));
   __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
-  s_tile(Ks[0], sa);
+  s_tile(Ks(Even{}), sa);
   {
     const bool mk = tile_masked(0);
 #pragma unroll
@@ -326,16 +348,17 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       update_ref(qb, mk ? max_masked(sa[qb], 0, qrow_of(qb)) : max_plain(sa[qb]));
   }
   // Two steps per trip so that S(t) and S(t+1) swap registers without copies.
+  // t stays even, so the parity of each call is known.
   int t = 0;
   for (; t + 2 < n_kt; t += 2) {
-    step(t, sa, sb);
-    step(t + 1, sb, sa);
+    step(Even{}, t, sa, sb);
+    step(Odd{}, t + 1, sb, sa);
   }
   if (t + 2 == n_kt) {
-    step(t, sa, sb);
-    last_step(t + 1, sb);
+    step(Even{}, t, sa, sb);
+    last_step(Odd{}, sb);
   } else {
-    last_step(t, sa);
+    last_step(Even{}, sa);
   }
 
 #pragma unroll
