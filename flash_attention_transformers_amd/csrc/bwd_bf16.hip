@@ -83,11 +83,70 @@ void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __
 }
 
 // ----------------------------------------------------------------------------
-// ----------------------------------------------------------------------------
 // 2. dK/dV
 constexpr int DKDV_THREADS = 512;  // 4 key slices x 2 roles
-constexpr int DKDV_NBUF = 2;       // Q/dO tiles: the current one and the next
 
+// Direct global -> LDS copy of one query tile for the dK/dV walk: BWD_BMQ rows
+// of Q and of dO in the SwzTile layout (swizzle applied on the global side,
+// as in DqKvCopy), then the tile's BWD_BMQ log-sum-exp and Dlt values.  Rows
+// past Sq load as zeros: their P is then finite and their dO, dP, Dlt and dS
+// are zero, so they add nothing.
+template <int D>
+struct DkdvCopy {
+  static constexpr int P = SwzTile<D>::P;
+  static constexpr int SLOTS_PER_ROW = P / 8;
+  static constexpr int TILE_SLOTS = BWD_BMQ * SLOTS_PER_ROW;  // per tensor
+  static constexpr int ROUNDS = 2 * TILE_SLOTS / DKDV_THREADS;
+  static constexpr int TILE_ELEMS = TILE_SLOTS * 8;             // bf16 per tensor
+  static constexpr int LSE_OFF = 2 * TILE_SLOTS * 16;           // bytes
+  static constexpr int DLT_OFF = LSE_OFF + BWD_BMQ * 4;
+  static constexpr int SINK_OFF = DLT_OFF + BWD_BMQ * 4;         // zeros from the other waves
+  static constexpr int BUF_BYTES = SINK_OFF + BWD_BMQ * 4;
+  static_assert(2 * TILE_SLOTS % DKDV_THREADS == 0 && TILE_SLOTS % 64 == 0, "whole rounds");
+  static_assert(BWD_BMQ == 64, "one 4-byte copy per lane for LSE and Dlt");
+  uint32_t off[ROUNDS];
+  int w0;  // first slot of this wave in round 0 (scalar)
+  __device__ __forceinline__ void init(int tid) {
+    w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int q = r * DKDV_THREADS + tid;
+      const int qq = q % TILE_SLOTS;
+      const int row = qq / SLOTS_PER_ROW, pos = qq - row * SLOTS_PER_ROW;
+      const int ch = pos ^ ((row >> 2) & 3);
+      off[r] = pos < D / 8 ? (uint32_t)(row * D + ch * 8) * 2 : 0x80000000u;
+    }
+  }
+  // Descriptors start at the tile's first row and end at Sq.
+  __device__ __forceinline__ void load(const Buf& q, const Buf& dout, const Buf& lse,
+                                       const Buf& dlt, char* buf, int lane) const {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      const int q0 = r * DKDV_THREADS + w0;
+      ld16_to_lds(q0 < TILE_SLOTS ? q : dout, off[r], buf + q0 * 16);
+    }
+    // Wave 0 copies the LSE values, wave 1 the Dlt values; the other waves
+    // issue the same copy with an empty descriptor into a sink, so that the
+    // copy is not under a branch.
+    const bool w_lse = w0 == 0, w_dlt = w0 == 64;
+    Buf src = w_lse ? lse : dlt;
+    if (!w_lse && !w_dlt) src.r = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
+    ld4_to_lds(src, lane * 4, buf + (w_lse ? LSE_OFF : w_dlt ? DLT_OFF : SINK_OFF));
+  }
+};
+
+// One workgroup per 128 keys of one KV head (or per chunk of the query range
+// for short KV), 8 waves: four 32-key slices, each served by a P-wave and a
+// dS-wave on the same SIMD.  The walk goes over every query tile of every
+// query head of the group; tile it arrives by direct copies two steps ahead
+// into buffer it % 3 (each buffer its own LDS object, so reads never wait for
+// copies in flight to the others).  One barrier per step:
+//   P-wave : S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e) -> P (bf16) to LDS
+//            | barrier |  dV^T += dO^T P
+//   dS-wave: dK^T += Q(it-1)^T dS(it-1), dP = dO V^T
+//            | barrier |  dS = P (dP - Dlt)
+// The P hand-off is double-buffered by step parity, so a P-wave may run into
+// the next step while its dS-wave still reads the previous P.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DKDV_THREADS)
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
@@ -99,17 +158,28 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   constexpr int BMQ = BWD_BMQ;            // query rows per step (two 32-row sub-blocks)
   constexpr int NSUB = BMQ / 32;
   using SW = SwzTile<D>;
-  constexpr int SP = SW::P;
-  constexpr int CH = BMQ * D / 8 / DKDV_THREADS;  // 16-byte chunks per thread per tensor
-  static_assert(CH >= 1 && (BMQ * D / 8) % DKDV_THREADS == 0, "tile loader must tile the workgroup");
-  // Q and dO tiles in the swizzled layout, double-buffered: step t reads
-  // tiles t and t+1.  Row and transposed reads (dO^T, Q^T) use the same copy.
-  __shared__ __attribute__((aligned(16))) bf16 Qs[DKDV_NBUF][BMQ * SP];
-  __shared__ __attribute__((aligned(16))) bf16 dOs[DKDV_NBUF][BMQ * SP];
-  // P handed from each P-wave to its dS-wave: [slice][sub-block][blk][lane][4].
-  __shared__ __attribute__((aligned(16))) float Pex[4 * NSUB * 4 * 64 * 4];
-  __shared__ __attribute__((aligned(16))) float lse_s[DKDV_NBUF][BMQ];
-  __shared__ __attribute__((aligned(16))) float dlt_s[DKDV_NBUF][BMQ];
+  using Copy = DkdvCopy<D>;
+  __shared__ __attribute__((aligned(16))) char QT0[Copy::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char QT1[Copy::BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char QT2[Copy::BUF_BYTES];
+  // P handed from each P-wave to its dS-wave, by step parity:
+  // [parity][slice][sub-block][lane][16 bf16].
+  constexpr int PEX_PAR = 4 * NSUB * 64 * 16;
+  __shared__ __attribute__((aligned(16))) bf16 Pex[2 * PEX_PAR];
+  auto QTbuf = [&](auto b) __attribute__((always_inline)) -> char* {
+    constexpr int i = decltype(b)::value % 3;
+    if constexpr (i == 0) return QT0; else if constexpr (i == 1) return QT1; else return QT2;
+  };
+  auto Qs = [](char* buf) __attribute__((always_inline)) { return reinterpret_cast<const bf16*>(buf); };
+  auto dOs = [](char* buf) __attribute__((always_inline)) {
+    return reinterpret_cast<const bf16*>(buf) + Copy::TILE_ELEMS;
+  };
+  auto lse_s = [](char* buf) __attribute__((always_inline)) {
+    return reinterpret_cast<const float*>(buf + Copy::LSE_OFF);
+  };
+  auto dlt_s = [](char* buf) __attribute__((always_inline)) {
+    return reinterpret_cast<const float*>(buf + Copy::DLT_OFF);
+  };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
@@ -118,31 +188,31 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int Hkv = Hq / G;
 
   // XCD-aware order: consecutive workgroup ids go round-robin to the 8 XCDs,
-  // so remap them so each XCD walks a contiguous run of (KV head, key tile,
-  // chunk) ids; the key tiles of one KV head then read the same Q/dO tiles
-  // through one L2.
+  // so remap them so each XCD keeps a fixed set of KV heads, whose key tiles
+  // then read the same Q/dO tiles through one L2.  Causal walks shrink with
+  // the key tile (key tile kt sees the queries from kt*128 on), so there each
+  // XCD takes its heads' key tiles in ascending order, longest walks first;
+  // otherwise each XCD walks a contiguous run of (KV head, key tile, chunk).
   const int nblk = gridDim.x;
-  const int L = ((nblk & 7) == 0) ? (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  const int split = L % nsplit;
-  const int rest = L / nsplit;
-  const int kt = rest % n_kt;
-  const int bkv = rest / n_kt;
+  const int nbkv = nblk / (n_kt * nsplit);
+  int split, kt, bkv;
+  if (CAUSAL && nsplit == 1 && (nbkv & 7) == 0) {
+    const int per = nbkv >> 3, j = blockIdx.x >> 3;
+    split = 0;
+    kt = j / per;
+    bkv = (blockIdx.x & 7) * per + j % per;
+  } else {
+    const int L = ((nblk & 7) == 0) ? (blockIdx.x & 7) * (nblk >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    split = L % nsplit;
+    const int rest = L / nsplit;
+    kt = rest % n_kt;
+    bkv = rest / n_kt;
+  }
   const int b = bkv / Hkv, kvh = bkv % Hkv;
   const int k0 = kt * BWD_BN;
   const int kw0 = k0 + slice * 32;
   const int key = kw0 + l32;
   const int diag = Skv - Sq;
-
-  // The P-wave keeps K of its slice, the dS-wave keeps V, as MFMA B operands.
-  const size_t kv_off = (size_t)bkv * Skv * D;
-  const Buf kvbuf(pwave ? K + kv_off : V + kv_off, (uint32_t)Skv * D * 2);
-  bf16x8 kvf[D / 16];
-#pragma unroll
-  for (int st = 0; st < D / 16; ++st)
-    kvf[st] = as_bf16x8(kvbuf.ld16((uint32_t)(key * D + 16 * st + 8 * g) * 2));
-  f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave)
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) acc[db] = zero_f32x16();
 
   // Query range of this chunk (q_chunk is a multiple of BMQ).
   const int qs = split * q_chunk;
@@ -154,54 +224,47 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   const int nq = qe > q_lo ? (qe - q_lo + BMQ - 1) / BMQ : 0;
   const int n_it = G * nq;  // steps: query tiles of every head of the group, heads ascending
-  auto qt0_of = [&](int it) { return q_lo + (it % nq) * BMQ; };
+  auto qt0_of = [&](int it) __attribute__((always_inline)) { return q_lo + (it % nq) * BMQ; };
 
-  uint4 qreg[CH], doreg[CH];
-  float pre_lse = 0.f, pre_dlt = 0.f;
-  auto load_it = [&](int it) {
-    const int r = it / nq;
-    const int h = kvh * G + r;
+  Copy cp;
+  cp.init(tid);
+  auto issue = [&](int it, char* dst) __attribute__((always_inline)) {
+    const int h = kvh * G + it / nq;
     const int qt0 = qt0_of(it);
-    const size_t hoff = (size_t)(b * Hq + h) * Sq;
-    // Rows at or past Sq fall outside the descriptors and load as zeros.
-    const Buf qbuf(Q + hoff * D, (uint32_t)Sq * D * 2);
-    const Buf dobuf(dO + hoff * D, (uint32_t)Sq * D * 2);
-#pragma unroll
-    for (int r2 = 0; r2 < CH; ++r2) {
-      const int ch = tid + DKDV_THREADS * r2;
-      const uint32_t off = (uint32_t)((qt0 + ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2;
-      qreg[r2] = qbuf.ld16(off);
-      doreg[r2] = dobuf.ld16(off);
-    }
-    const Buf lbuf(LSE + hoff, (uint32_t)Sq * 4);
-    const Buf dbuf(DLT + hoff, (uint32_t)Sq * 4);
-    if (tid < BMQ) {
-      pre_lse = lbuf.ldf((uint32_t)(qt0 + tid) * 4);
-      pre_dlt = dbuf.ldf((uint32_t)(qt0 + tid) * 4);
-    }
+    const size_t row0 = (size_t)(b * Hq + h) * Sq + qt0;
+    const uint32_t rows = (uint32_t)(Sq - qt0);
+    cp.load(Buf(Q + row0 * D, rows * D * 2), Buf(dO + row0 * D, rows * D * 2),
+            Buf(LSE + row0, rows * 4), Buf(DLT + row0, rows * 4), dst, lane);
   };
-  auto store_it = [&](int it, int buf) {
-#pragma unroll
-    for (int r2 = 0; r2 < CH; ++r2) {
-      const int ch = tid + DKDV_THREADS * r2;
-      const int off = SW::store_off(ch / (D / 8), ch % (D / 8));
-      *reinterpret_cast<uint4*>(&Qs[buf][off]) = qreg[r2];
-      *reinterpret_cast<uint4*>(&dOs[buf][off]) = doreg[r2];
-    }
-    if (tid < BMQ) {
-      // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
-      const bool real = qt0_of(it) + tid < Sq;
-      lse_s[buf][tid] = real ? pre_lse * MATTN_LOG2E : MATTN_INF;
-      dlt_s[buf][tid] = real ? pre_dlt : 0.f;
-    }
-  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
+  using B2 = std::integral_constant<int, 2>;
 
-  float* pex = Pex + slice * (NSUB * 4 * 64 * 4);
+  // The P-wave keeps K of its slice, the dS-wave keeps V, as MFMA B operands.
+  const size_t kv_off = (size_t)bkv * Skv * D;
+  const Buf kvbuf(pwave ? K + kv_off : V + kv_off, (uint32_t)Skv * D * 2);
+  bf16x8 kvf[D / 16];
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    kvf[st] = as_bf16x8(kvbuf.ld16((uint32_t)(key * D + 16 * st + 8 * g) * 2));
+  if (n_it > 0) issue(0, QTbuf(B0{}));
+  if (n_it > 1) issue(1, QTbuf(B1{}));
+  // Everything issued so far has landed before the walk starts, so that no
+  // wait for these loads ends up inside the loop, where it would also wait
+  // for the copies of later tiles.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  f32x16 acc[D / 32];  // dV^T (P-wave) or dK^T (dS-wave)
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) acc[db] = zero_f32x16();
+
   SW sw;
   sw.init(lane);
+  // This lane's 32 bytes of the P hand-off for sub-block 0 of parity 0.
+  int pex_lane = (slice * NSUB * 64 + lane) * 16;
+  asm volatile("" : "+v"(pex_lane));
   // S = Q K^T (P-wave) or dP = dO V^T (dS-wave) for one tile: lane = key
   // column, registers = query rows; both sub-blocks as independent chains.
-  auto score_tile = [&](const bf16* tile, f32x16 (&sc)[NSUB]) {
+  auto score_tile = [&](const bf16* tile, f32x16 (&sc)[NSUB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < NSUB; ++qb) sc[qb] = zero_f32x16();
 #pragma unroll
@@ -210,10 +273,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       for (int qb = 0; qb < NSUB; ++qb)
         sc[qb] = mfma32(sw.row(tile, qb * 32, st), kvf[st], sc[qb]);
   };
-  // P = 2^(S*c - LSE*log2e), masked above the causal diagonal; P goes to
-  // the dS-wave through LDS and stays in registers as bf16 for dV.
+  // P = 2^(S*c - LSE*log2e), masked above the causal diagonal; P (bf16)
+  // stays in registers for dV and goes to the dS-wave through LDS.
   bf16x8 pb[NSUB][2];
-  auto exp_tile = [&](auto masked, int buf, int qt0, const f32x16 (&sc)[NSUB]) {
+  auto exp_tile = [&](auto masked, const float* lse, bf16* pex, int qt0,
+                      const f32x16 (&sc)[NSUB]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
 #pragma unroll
     for (int qb = 0; qb < NSUB; ++qb) {
@@ -222,120 +286,113 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       const int y = key - diag - qt0 - qb * 32 - 4 * g;
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const f32x4 Lv = *reinterpret_cast<const f32x4*>(&lse_s[buf][qb * 32 + 8 * blk + 4 * g]);
-        f32x4 pv;
+        const f32x4 Lv = *reinterpret_cast<const f32x4*>(&lse[qb * 32 + 8 * blk + 4 * g]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * blk + j;
-          float pr = fast_exp2(__builtin_fmaf(sc[qb][i], c, -Lv[j]));
+          float pr = fast_exp2(__builtin_fmaf(sc[qb][i], c, -Lv[j] * MATTN_LOG2E));
           if (MASK && y > 8 * blk + j) pr = 0.f;
-          pv[j] = pr;
           pb[qb][i >> 3][i & 7] = (bf16)pr;
         }
-        *reinterpret_cast<f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]) = pv;
       }
+      *reinterpret_cast<bf16x8*>(pex + qb * 64 * 16) = pb[qb][0];
+      *reinterpret_cast<bf16x8*>(pex + qb * 64 * 16 + 8) = pb[qb][1];
     }
   };
   // dV^T += dO^T P.
-  auto dv_tile = [&](int buf) {
+  auto dv_tile = [&](const bf16* dos) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < NSUB; ++qb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         bf16x8 a[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          a[db] = sw.trans(dOs[buf], qb * 32 + 16 * t, db);
+        for (int db = 0; db < D / 32; ++db) a[db] = sw.trans(dos, qb * 32 + 16 * t, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], pb[qb][t], acc[db]);
       }
   };
   // dS = P (dP - Dlt), rounded to bf16 as the B operand of dK^T += Q^T dS.
-  auto ds_tile = [&](int buf, const f32x16 (&dp)[NSUB], bf16x8 (&dsb)[NSUB][2]) {
+  auto ds_tile = [&](const float* dlt, const bf16* pex, const f32x16 (&dp)[NSUB],
+                     bf16x8 (&dsb)[NSUB][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qb = 0; qb < NSUB; ++qb)
+    for (int qb = 0; qb < NSUB; ++qb) {
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pex + qb * 64 * 16);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pex + qb * 64 * 16 + 8);
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
-        const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt_s[buf][qb * 32 + 8 * blk + 4 * g]);
-        const f32x4 pv = *reinterpret_cast<const f32x4*>(&pex[((qb * 4 + blk) * 64 + lane) * 4]);
+        const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt[qb * 32 + 8 * blk + 4 * g]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * blk + j;
-          dsb[qb][i >> 3][i & 7] = (bf16)(pv[j] * (dp[qb][i] - Dl[j]));
+          const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
+          dsb[qb][i >> 3][i & 7] = (bf16)(pv * (dp[qb][i] - Dl[j]));
         }
       }
+    }
   };
-  auto dk_tile = [&](int buf, const bf16x8 (&dsb)[NSUB][2]) {
+  auto dk_tile = [&](const bf16* qs_, const bf16x8 (&dsb)[NSUB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < NSUB; ++qb)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         bf16x8 a[D / 32];
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          a[db] = sw.trans(Qs[buf], qb * 32 + 16 * t, db);
+        for (int db = 0; db < D / 32; ++db) a[db] = sw.trans(qs_, qb * 32 + 16 * t, db);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) acc[db] = mfma32(a[db], dsb[qb][t], acc[db]);
       }
   };
 
-  // The dS-wave runs one step behind the P-wave, so that on every SIMD (which
-  // holds the P-wave and the dS-wave of one slice) MFMA work of one wave
-  // meets VALU work of the other.  Step t, with tile t in buffer t&1 and tile
-  // t-1 in the other:
-  //   phase A: P-wave S(t) = Q K^T        | dS-wave dK^T += Q(t-1)^T dS(t-1)
-  //   phase B: P-wave P(t) = exp, to LDS  | dS-wave dP(t) = dO V^T
-  //   -- barrier: P(t) published --
-  //   phase C: P-wave dV^T += dO^T P(t)   | dS-wave dS(t) = P (dP - Dlt)
-  //            everyone stores tile t+1 (prefetched a step earlier) over
-  //            tile t-1, which phase A was the last to read
-  //   -- barrier: tile t+1 published --
-  // The buffer parity is a compile-time constant of each unrolled step.
-  f32x16 sc[NSUB];       // S(t) on the P-wave, dP(t) on the dS-wave
-  bf16x8 dsb[NSUB][2];   // dS(t-1), dS-wave only
-  auto step = [&](auto parity, int it) {
-    constexpr int b0 = decltype(parity)::value, b1 = b0 ^ 1;
+  // Step it, tile it in buffer it % 3 (a compile-time constant of each
+  // unrolled step), tile it-1 in buffer (it+2) % 3.  The barrier publishes
+  // P(it) (the fence of __syncthreads waits for the LDS writes) and, since
+  // every wave has first waited for its own copies (vmcnt(0): the fence does
+  // not cover direct copies), tile it+1; it also ends every read of tile
+  // it-1, whose buffer then takes tile it+2.
+  f32x16 sc[NSUB];       // S(it) on the P-wave, dP(it) on the dS-wave
+  bf16x8 dsb[NSUB][2];   // dS(it-1), dS-wave only
+  auto step = [&](auto bsel, int it) __attribute__((always_inline)) {
+    constexpr int bi = decltype(bsel)::value;
+    char* cur = QTbuf(bsel);
+    char* prev = QTbuf(std::integral_constant<int, bi + 2>{});
+    bf16* pex = Pex + (it & 1) * PEX_PAR + pex_lane;
     if (pwave) {
-      score_tile(Qs[b0], sc);
+      score_tile(Qs(cur), sc);
       const int qt0 = qt0_of(it);
       if (CAUSAL && (kw0 + 31 > qt0 + diag))
-        exp_tile(std::true_type{}, b0, qt0, sc);
+        exp_tile(std::true_type{}, lse_s(cur), pex, qt0, sc);
       else
-        exp_tile(std::false_type{}, b0, qt0, sc);
+        exp_tile(std::false_type{}, lse_s(cur), pex, qt0, sc);
     } else {
-      if (it > 0) dk_tile(b1, dsb);
-      score_tile(dOs[b0], sc);
+      if (it > 0) dk_tile(Qs(prev), dsb);
+      score_tile(dOs(cur), sc);
     }
-    __syncthreads();  // P(it) is in Pex
-    if (it + 1 < n_it) {
-      store_it(it + 1, b1);
-      if (it + 2 < n_it) load_it(it + 2);
-    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+    __syncthreads();
+    if (it + 2 < n_it) issue(it + 2, prev);
     if (pwave)
-      dv_tile(b0);
+      dv_tile(dOs(cur));
     else
-      ds_tile(b0, sc, dsb);
-    __syncthreads();  // tile it+1 is visible; Pex may be rewritten
+      ds_tile(dlt_s(cur), pex, sc, dsb);
   };
 
-  if (n_it > 0) {
-    load_it(0);
-    store_it(0, 0);
-    if (n_it > 1) load_it(1);
-    __syncthreads();
-  }
+  if (n_it > 0) __syncthreads();  // tiles 0 and 1 landed everywhere (waited for above)
   int it = 0;
-  for (; it + 1 < n_it; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    step(std::integral_constant<int, 1>{}, it + 1);
+  for (; it + 3 <= n_it; it += 3) {
+    step(B0{}, it);
+    step(B1{}, it + 1);
+    step(B2{}, it + 2);
   }
-  if (it < n_it) step(std::integral_constant<int, 0>{}, it);
+  if (it < n_it) step(B0{}, it);
+  if (it + 1 < n_it) step(B1{}, it + 1);
   // The dS-wave's last dK uses the last tile, still in place.
   if (!pwave && n_it > 0) {
-    if ((n_it - 1) & 1)
-      dk_tile(1, dsb);
-    else
-      dk_tile(0, dsb);
+    switch ((n_it - 1) % 3) {
+      case 0: dk_tile(Qs(QTbuf(B0{})), dsb); break;
+      case 1: dk_tile(Qs(QTbuf(B1{})), dsb); break;
+      default: dk_tile(Qs(QTbuf(B2{})), dsb); break;
+    }
   }
 
   if (key >= Skv) return;

@@ -216,6 +216,11 @@ __device__ __forceinline__ void ld16_to_lds(const Buf& b, uint32_t off, void* ld
   __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)lds_base, 16,
                                            off, 0, 0, 0);
 }
+// The same with 4 bytes per lane: lane L's word lands at lds_base + 4 L.
+__device__ __forceinline__ void ld4_to_lds(const Buf& b, uint32_t off, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(b.r, (__attribute__((address_space(3))) void*)lds_base, 4,
+                                           off, 0, 0, 0);
+}
 
 // A tile of `ROWS` rows x D bf16 with row pitch PITCH (elements), filled by
 // ld16_to_lds.  The tile's LDS bytes are split into 16-byte slots, slot q =
