@@ -291,31 +291,33 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       asm volatile("" : "+v"(rs[qb][0]), "+v"(rs[qb][1]), "+v"(rs[qb][2]), "+v"(rs[qb][3]));
       l[qb] += (rs[qb][0] + rs[qb][1]) + (rs[qb][2] + rs[qb][3]);
     }
-    // Phase 2: the MFMAs of O += P(t) V(t) with the row max of S(t+1).
+    // Phase 2: the MFMAs of O += P(t) V(t) with the row max of S(t+1).  Each
+    // V^T fragment is two transposed reads; they run four fragments ahead of
+    // the MFMA that uses them (two fragments ahead measured 3-6% slower).
     float mx[QB];
     if (tile_masked(t + 1)) {
       pv_tile(Vs(p0));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = max_masked(nxt[qb], t + 1, qrow_of(qb));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
       for (int i = 0; i < NMF; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     } else {
       pv_tile(Vs(p0));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) mx[qb] = max_plain(nxt[qb]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
       for (int i = 0; i < NMF; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
 #pragma unroll
