@@ -457,10 +457,10 @@ void bwd_reduce_kernel(const float* __restrict__ part, bf16* __restrict__ dK,
 
 // ----------------------------------------------------------------------------
 // 3. dQ
-constexpr int DQ_SLICES = 2;               // 32-row query slices per workgroup
-constexpr int DQ_BM = 32 * DQ_SLICES;      // query rows per workgroup
+constexpr int DQ_WAVES = 4;                // one 32-row query slice per wave
+constexpr int DQ_BM = 32 * DQ_WAVES;       // query rows per workgroup
 constexpr int DQ_BN = 64;                  // keys per tile
-constexpr int DQ_THREADS = 128 * DQ_SLICES;  // DQ_SLICES query slices x 2 key halves
+constexpr int DQ_THREADS = 64 * DQ_WAVES;
 
 // Direct global -> LDS copy of one K tile and one V tile (DQ_BN rows each)
 // into one buffer laid out as [K tile | V tile], both in the SwzTile layout.
@@ -477,37 +477,47 @@ struct DqKvCopy {
   static constexpr int ROUNDS = 2 * TILE_SLOTS / DQ_THREADS;
   static constexpr int BUF_ELEMS = 2 * TILE_SLOTS * 8;
   static_assert(2 * TILE_SLOTS % DQ_THREADS == 0 && TILE_SLOTS % 64 == 0, "whole rounds");
-  uint32_t off[ROUNDS];
+  // Per-round byte offsets within a tile are below 2^15, so two share a
+  // register (a register each would not fit beside the kernel's other state);
+  // 0xffff marks a pad slot and lies past every tile's descriptor, so it
+  // loads zeros.
+  static_assert(DQ_BN * D * 2 < 0xffff, "16-bit offsets");
+  uint32_t off2[(ROUNDS + 1) / 2];
   int w0;  // first slot of this wave in round 0 (scalar)
   __device__ __forceinline__ void init(int tid) {
     w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+#pragma unroll
+    for (int r = 0; r < (ROUNDS + 1) / 2; ++r) off2[r] = 0xffffffffu;
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
       const int q = r * DQ_THREADS + tid;
       const int qq = q % TILE_SLOTS;  // slot within its tensor's tile
       const int row = qq / SLOTS_PER_ROW, pos = qq - row * SLOTS_PER_ROW;
       const int ch = pos ^ ((row >> 2) & 3);
-      off[r] = pos < D / 8 ? (uint32_t)(row * D + ch * 8) * 2 : 0x80000000u;
+      const uint32_t o = pos < D / 8 ? (uint32_t)(row * D + ch * 8) * 2 : 0xffffu;
+      off2[r / 2] = (r & 1) ? ((off2[r / 2] & 0xffffu) | (o << 16)) : ((off2[r / 2] & 0xffff0000u) | o);
     }
   }
-  // Tile rows start at the descriptors' bases; rows past their ends load zeros.
+  // The descriptors cover exactly the tile's rows (fewer at the end of the
+  // keys); rows past them, and pad slots, load zeros.
   __device__ __forceinline__ void load(const Buf& k, const Buf& v, bf16* buf) const {
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
       const int q0 = r * DQ_THREADS + w0;
-      ld16_to_lds(q0 < TILE_SLOTS ? k : v, off[r], buf + q0 * 8);
+      const uint32_t o = (r & 1) ? (off2[r / 2] >> 16) : (off2[r / 2] & 0xffffu);
+      ld16_to_lds(q0 < TILE_SLOTS ? k : v, o, buf + q0 * 8);
     }
   }
 };
 
 // dQ_i = scale * sum_j dS_ij K_j for a block of DQ_BM query rows.  Each wave
-// keeps its 32 rows of Q and dO in registers and takes one 32-key half of
-// every 64-key tile.  K/V tiles arrive by direct copies into two LDS
+// keeps its 32 rows of Q and dO in registers and walks every 64-key tile in
+// two 32-key halves.  K/V tiles arrive by direct copies into two LDS
 // buffers, one tile ahead, with one barrier per tile.  Each buffer is its own
 // LDS object, so reads of the current tile never wait for the copies in
-// flight to the other.  Small workgroups let two of them share a CU: the two
-// waves on a SIMD then belong to different workgroups and drift out of phase,
-// so the VALU work of one (dS) overlaps the MFMA work of the other.
+// flight to the other.  Two workgroups share a CU: the two waves on a SIMD
+// then belong to different workgroups and drift out of phase, so the VALU
+// work of one (dS) overlaps the MFMA work of the other.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DQ_THREADS, 2)
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
@@ -527,8 +537,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int slice = wave % DQ_SLICES;  // 32 query rows
-  const int kh = wave / DQ_SLICES;     // which 32-key half of every tile this wave takes
+  const int slice = wave;  // 32 query rows
   int bh, qt;
   tile_of_block(blockIdx.x, gridDim.x / n_qt, n_qt, CAUSAL, bh, qt);
   const int h = bh % Hq, b = bh / Hq;
@@ -551,7 +560,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const bf16* Vh = V + kv_off;
   auto issue = [&](int kt, bf16* dst) __attribute__((always_inline)) {
     const int j0 = kt * DQ_BN;
-    const uint32_t nb = (uint32_t)(Skv - j0) * D * 2;
+    const uint32_t nb = (uint32_t)min(DQ_BN, Skv - j0) * D * 2;
     cp.load(Buf(Kh + (size_t)j0 * D, nb), Buf(Vh + (size_t)j0 * D, nb), dst);
   };
   using B0 = std::integral_constant<int, 0>;
@@ -570,22 +579,21 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const float lse2 = qrow < Sq ? LSE[(size_t)bh * Sq + qrow] * MATTN_LOG2E : MATTN_INF;
   const float dl = qrow < Sq ? DLT[(size_t)bh * Sq + qrow] : 0.f;
 
-  f32x16 adq[D / 32];  // partial dQ^T over this wave's key halves
+  f32x16 adq[D / 32];  // dQ^T of this wave's 32 rows
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) adq[db] = zero_f32x16();
 
-  const int kb0 = kh * 32;  // this wave's 32 keys of the tile
   // Tile kt sits in buffer kt & 1.  At its top this thread's copies of tile
   // kt have landed; the barrier makes that true for everyone and ends every
   // read of tile kt-1, whose buffer then takes tile kt+1.
-  auto tile = [&](auto bsel, int kt) __attribute__((always_inline)) {
+  auto tile = [&](auto bsel, auto tail, int kt) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     barrier_keep_copies();
     if (kt + 1 < n_kt) issue(kt + 1, KVbuf(std::integral_constant<int, decltype(bsel)::value ^ 1>{}));
     const bf16* Ks = KVbuf(bsel);
     const bf16* Vs = Ks + VOFF;
     const int j0 = kt * DQ_BN;
-    auto step = [&](auto masked) __attribute__((always_inline)) {
+    auto step = [&](auto masked, int kb0) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(masked)::value;
       f32x16 s = zero_f32x16(), dp = zero_f32x16();
 #pragma unroll
@@ -622,45 +630,47 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         for (int db = 0; db < D / 32; ++db) adq[db] = mfma32(a[db], dsb[t], adq[db]);
       }
     };
-    const bool masked = (j0 + kb0 + 32 > Skv) || (CAUSAL && (j0 + kb0 + 31 > qw0 + diag));
-    if (masked)
-      step(std::true_type{});
-    else
-      step(std::false_type{});
+#pragma unroll
+    for (int kb0 = 0; kb0 < DQ_BN; kb0 += 32) {
+      // Only tiles that reach past Skv (the last one at most) test for it, and
+      // only outside the main loop, so the loop body holds at most the causal
+      // variant.
+      if constexpr (decltype(tail)::value) {
+        if (j0 + kb0 >= Skv) break;  // no key of this half exists
+        step(std::true_type{}, kb0);
+      } else {
+        if (CAUSAL && (j0 + kb0 + 31 > qw0 + diag))
+          step(std::true_type{}, kb0);
+        else
+          step(std::false_type{}, kb0);
+      }
+      // One half at a time: interleaving the halves needs more registers
+      // than two waves per SIMD have.
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
+  // Tiles wholly below Skv run in the loop, two per trip so that each
+  // buffer is named at compile time; the rest (at most two, starting on an
+  // even tile) also check for keys past Skv.
+  const int n_full = Skv % DQ_BN == 0 ? n_kt : min(n_kt, Skv / DQ_BN);
   int kt = 0;
-  for (; kt + 2 <= n_kt; kt += 2) {
-    tile(B0{}, kt);
-    tile(B1{}, kt + 1);
+  for (; kt + 2 <= n_full; kt += 2) {
+    tile(B0{}, std::false_type{}, kt);
+    tile(B1{}, std::false_type{}, kt + 1);
   }
-  if (kt < n_kt) tile(B0{}, kt);
+  if (kt < n_kt) tile(B0{}, std::true_type{}, kt);
+  if (kt + 1 < n_kt) tile(B1{}, std::true_type{}, kt + 1);
 
-  // Sum the two key-half partials in a fixed order (half 0 + half 1) through
-  // LDS, reusing the first tile buffer, and write dQ.
-  constexpr int RED_FLOATS = (D / 32) * 16 * 64;  // per slice
-  static_assert(DQ_SLICES * RED_FLOATS * 4 <= Copy::BUF_ELEMS * 2, "partials fit in one buffer");
-  __syncthreads();
-  float* red_slice = reinterpret_cast<float*>(KV0) + slice * RED_FLOATS;
-  if (kh == 1) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; i += 4)
-        *reinterpret_cast<f32x4*>(&red_slice[((db * 4 + i / 4) * 64 + lane) * 4]) =
-            f32x4{adq[db][i], adq[db][i + 1], adq[db][i + 2], adq[db][i + 3]};
-  }
-  __syncthreads();
-  if (kh == 0 && qrow < Sq) {
+  if (qrow < Sq) {
     bf16* prow = dQ + ((size_t)bh * Sq + qrow) * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const f32x4 o = *reinterpret_cast<const f32x4*>(&red_slice[((db * 4 + r) * 64 + lane) * 4]);
         const int d = db * 32 + r * 8 + g * 4;
         uint2 w;
-        w.x = pack_bf16x2((adq[db][4 * r] + o[0]) * scale, (adq[db][4 * r + 1] + o[1]) * scale);
-        w.y = pack_bf16x2((adq[db][4 * r + 2] + o[2]) * scale, (adq[db][4 * r + 3] + o[3]) * scale);
+        w.x = pack_bf16x2(adq[db][4 * r] * scale, adq[db][4 * r + 1] * scale);
+        w.y = pack_bf16x2(adq[db][4 * r + 2] * scale, adq[db][4 * r + 3] * scale);
         *reinterpret_cast<uint2*>(prow + d) = w;
       }
   }
