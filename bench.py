@@ -3,8 +3,10 @@
 One step = mattn_fwd + the backward (D = sum(dO*O) preprocess, dK/dV kernel,
 dQ kernel) over one batch of seeded synthetic input that is already resident
 in HBM.  The backward is enqueued as its three stages (mattn_bwd_stages, the
-same kernels mattn_bwd issues, in the same order on the same stream) so that
-HIP events between them time each kernel inside the timed region.
+same kernels mattn_bwd issues, in the same order on the same stream).  The
+timed region holds exactly `steps` steps and nothing else; a second pass of
+the same steps with HIP events between the kernels gives the per-kernel
+times, and a pass of forwards alone gives the forward's share.
 
 Default workload: GQA causal training attention, B=4, Hq=32, Hkv=8, S=4096,
 D=128, bf16 (the long-sequence configuration that exercises every step of the
@@ -206,20 +208,25 @@ def main_paged(args, w):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for e in evs:
-        e[0].record(stream)
+    for _ in range(args.steps):
         step()
-        e[1].record(stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
+    # Per-call span (attention kernel plus merge): a second pass with events
+    # around each call.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for e in evs:
+        e[0].record(stream)
+        step()
+        e[1].record(stream)
+    torch.cuda.synchronize()
     call_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     flop = w.fwd_flop()
     value = flop / (ms_step * 1e-3) / 1e12
@@ -319,24 +326,41 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    nev = 2 + len(stages)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    # Timed region: exactly `steps` steps, nothing else on the stream.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
+    # Per-kernel breakdown: the same number of steps again, with an event
+    # between consecutive kernels.  Each event costs ~12 us of stream time at
+    # a kernel boundary, so these steps run a little longer than the timed
+    # ones; kernel_ms[k] is the span between the events around kernel k.
+    nev = 2 + len(stages)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
                for i, n in enumerate(names)}
-    fwd_ms = kern_ms["fwd"]
-    bwd_ms = sum(kern_ms[n] for n in names[1:])
+    # The forward alone, back to back (events only around the loop); the
+    # backward's share of the step is the rest.
+    f0 = torch.cuda.Event(enable_timing=True)
+    f1 = torch.cuda.Event(enable_timing=True)
+    f0.record(stream)
+    for _ in range(args.steps):
+        fa.mattn_fwd(q, k, v, o, lse, w.causal, w.scale, stream)
+    f1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = f0.elapsed_time(f1) / args.steps
+    bwd_ms = ms_step - fwd_ms
 
     fwd_flop = w.fwd_flop()
     step_flop = fwd_flop + (w.bwd_flop() if w.backward else 0.0)
@@ -386,6 +410,8 @@ def main():
         "bwd_pct_of_peak": None if bwd_tf is None else round(100 * bwd_tf / peak, 2),
         "fwd_ms": round(fwd_ms, 4),
         "bwd_ms": round(bwd_ms, 4),
+        "kernel_ms_note": "per-kernel spans from a second pass of the same steps with an event "
+                          "between kernels (about 12 us of event cost per kernel boundary)",
         "wall_s_timed_region": round(wall, 4),
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
         "roofline": roofline,
