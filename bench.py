@@ -1,9 +1,10 @@
 """Benchmark of the fused attention hot path on one MI355X.
 
-One step = mattn_fwd + the backward (D = sum(dO*O) preprocess, dK/dV kernel,
-dQ kernel) over one batch of seeded synthetic input that is already resident
-in HBM.  The backward is enqueued as its three stages (mattn_bwd_stages, the
-same kernels mattn_bwd issues, in the same order on the same stream).  The
+One step = mattn_fwd + the backward (the dQ kernel, which also forms
+D = sum(dO*O) for bf16, then the dK/dV kernel) over one batch of seeded
+synthetic input that is already resident in HBM.  The backward is enqueued as
+its stages (mattn_bwd_stages, the same kernels mattn_bwd issues, in the same
+order on the same stream).  The
 timed region holds exactly `steps` steps and nothing else; a second pass of
 the same steps with HIP events between the kernels gives the per-kernel
 times, and a pass of forwards alone gives the forward's share.
@@ -309,8 +310,14 @@ def main():
     ws = fa.bwd_workspace(q, k)
     stream = torch.cuda.current_stream(dev)
 
-    stages = [fa.MATTN_BWD_PREPROCESS, fa.MATTN_BWD_DKDV, fa.MATTN_BWD_DQ] if w.backward else []
-    names = ["fwd", "pre", "dkdv", "dq"][: 1 + len(stages)]
+    # The stages mattn_bwd enqueues: bf16 forms D inside the dQ kernel.
+    if not w.backward:
+        stages, names = [], ["fwd"]
+    elif w.dtype == "bf16":
+        stages, names = [fa.MATTN_BWD_DQ, fa.MATTN_BWD_DKDV], ["fwd", "dq", "dkdv"]
+    else:
+        stages = [fa.MATTN_BWD_PREPROCESS, fa.MATTN_BWD_DQ, fa.MATTN_BWD_DKDV]
+        names = ["fwd", "pre", "dq", "dkdv"]
 
     def step(ev=None):
         if ev is not None:

@@ -152,7 +152,9 @@ def mattn_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,
 def mattn_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, workspace, stages: int,
                      causal: bool = False, scale: Optional[float] = None, stream=None) -> None:
     """Enqueue only the selected backward stages (MATTN_BWD_* flags), in the
-    order preprocess, dK/dV, dQ; all three together are exactly mattn_bwd."""
+    order preprocess, dQ, dK/dV (separate calls follow the same order).  The
+    bf16 dQ stage also forms the per-row D itself, so mattn_bwd enqueues dQ
+    and dK/dV for bf16 and all three for fp32; the results are the same bits."""
     _require(q, k, v, o, lse, do, dq, dk, dv, workspace)
     B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
     if scale is None:

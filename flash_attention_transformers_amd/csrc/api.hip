@@ -111,22 +111,25 @@ mattn_status mattn_bwd_stages(const void* q, const void* k, const void* v, const
   float* dlt = (float*)workspace;
   float* part = (float*)((char*)workspace + dlt_bytes(B, Hq, Sq));
   const bool bf = dtype == MATTN_BF16;
+  // Selected stages run in the order preprocess, dQ, dK/dV.  The bf16 dQ
+  // kernel forms the per-row D itself and stores it, bitwise equal to the
+  // preprocess result; the fp32 dQ and both dK/dV kernels read it.
   if (stages & MATTN_BWD_PREPROCESS) {
     if (mattn::launch_bwd_preprocess(p, bf, o, dout, dlt, stream) != hipSuccess)
       return MATTN_ERR_LAUNCH;
+  }
+  if (stages & MATTN_BWD_DQ) {
+    const hipError_t e =
+        bf ? mattn::launch_dq_bf16(p, q, k, v, o, lse, dlt, dout, dq, stream)
+           : mattn::launch_dq_f32(p, (const float*)q, (const float*)k, (const float*)v, lse, dlt,
+                                  (const float*)dout, (float*)dq, stream);
+    if (e != hipSuccess) return MATTN_ERR_LAUNCH;
   }
   if (stages & MATTN_BWD_DKDV) {
     const hipError_t e =
         bf ? mattn::launch_dkdv_bf16(p, q, k, v, lse, dlt, dout, dk, dv, part, stream)
            : mattn::launch_dkdv_f32(p, (const float*)q, (const float*)k, (const float*)v, lse,
                                     dlt, (const float*)dout, (float*)dk, (float*)dv, stream);
-    if (e != hipSuccess) return MATTN_ERR_LAUNCH;
-  }
-  if (stages & MATTN_BWD_DQ) {
-    const hipError_t e =
-        bf ? mattn::launch_dq_bf16(p, q, k, v, lse, dlt, dout, dq, stream)
-           : mattn::launch_dq_f32(p, (const float*)q, (const float*)k, (const float*)v, lse, dlt,
-                                  (const float*)dout, (float*)dq, stream);
     if (e != hipSuccess) return MATTN_ERR_LAUNCH;
   }
   return MATTN_OK;
@@ -137,9 +140,11 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
                        int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
                        mattn_dtype dtype, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
+  // bf16: the dQ kernel forms D itself, so no separate preprocess pass.
+  const unsigned stages = dtype == MATTN_BF16 ? (MATTN_BWD_DQ | MATTN_BWD_DKDV)
+                                              : (MATTN_BWD_PREPROCESS | MATTN_BWD_DQ | MATTN_BWD_DKDV);
   return mattn_bwd_stages(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, causal,
-                          scale, dtype, workspace, workspace_bytes,
-                          MATTN_BWD_PREPROCESS | MATTN_BWD_DKDV | MATTN_BWD_DQ, stream);
+                          scale, dtype, workspace, workspace_bytes, stages, stream);
 }
 
 size_t mattn_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Sq, int D, int page_size,

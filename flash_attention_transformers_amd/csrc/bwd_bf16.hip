@@ -62,6 +62,38 @@ constexpr int THREADS = 256;
 
 // ----------------------------------------------------------------------------
 // 1. preprocess
+//
+// Dlt of one row in bf16: two half-rows, each the fp32 fma chain below over
+// the columns 16s + 8h .. 16s + 8h + 7 (s ascending) that one lane of the dQ
+// kernel holds, then the two halves added.  The dQ kernel forms Dlt with the
+// same steps (it already holds dO in that layout), so both give the same
+// bits and either may feed the dK/dV kernel.
+__device__ __forceinline__ float dlt_half_row_step(bf16x8 dout, bf16x8 o, float acc) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc = __builtin_fmaf((float)dout[e], (float)o[e], acc);
+  return acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(THREADS)
+void bwd_pre_bf16_kernel(const bf16* __restrict__ O, const bf16* __restrict__ dO,
+                         float* __restrict__ dlt, long long rows) {
+  // Two adjacent lanes per row, one per half.
+  const long long row = ((long long)blockIdx.x * THREADS + threadIdx.x) >> 1;
+  const int h = threadIdx.x & 1;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16* po = O + row * D + 8 * h;
+    const bf16* pd = dO + row * D + 8 * h;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      acc = dlt_half_row_step(*reinterpret_cast<const bf16x8*>(pd + 16 * s),
+                              *reinterpret_cast<const bf16x8*>(po + 16 * s), acc);
+  }
+  const float tot = acc + __shfl_xor(acc, 1);
+  if (h == 0 && row < rows) dlt[row] = tot;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(THREADS)
 void bwd_pre_kernel(const T* __restrict__ O, const T* __restrict__ dO, float* __restrict__ dlt,
@@ -545,10 +577,10 @@ struct DqKvCopy {
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(DQ_THREADS, 2)
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
-                   const bf16* __restrict__ V, const bf16* __restrict__ dO,
-                   const float* __restrict__ LSE, const float* __restrict__ DLT,
-                   bf16* __restrict__ dQ, int Hq, int G, int Sq, int Skv, float scale, float c,
-                   int n_qt) {
+                   const bf16* __restrict__ V, const bf16* __restrict__ O,
+                   const bf16* __restrict__ dO, const float* __restrict__ LSE,
+                   float* __restrict__ DLT, bf16* __restrict__ dQ, int Hq, int G, int Sq,
+                   int Skv, float scale, float c, int n_qt) {
   using SW = SwzTile<D>;
   using Copy = DqKvCopy<D>;
   constexpr int VOFF = Copy::TILE_SLOTS * 8;  // V tile's offset in a buffer (elements)
@@ -601,7 +633,18 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
   // A padded query row gets LSE = +inf, so its P (and dS) is exactly 0.
   const float lse2 = qrow < Sq ? LSE[(size_t)bh * Sq + qrow] * MATTN_LOG2E : MATTN_INF;
-  const float dl = qrow < Sq ? DLT[(size_t)bh * Sq + qrow] : 0.f;
+  // Dlt = sum_d dO * O of this lane's row: this lane's half of the row (the
+  // columns its dO fragments hold), then its partner lane's half.  The
+  // arithmetic is dlt_half_row's, so the value is bitwise the preprocess
+  // kernel's.  It is also stored for the dK/dV kernel, which runs after this
+  // one.  Rows past Sq load zeros and get 0.
+  const Buf obuf(O + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
+  float dhalf = 0.f;
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s)
+    dhalf = dlt_half_row_step(dof[s], as_bf16x8(obuf.ld16((uint32_t)(qrow * D + 16 * s + 8 * g) * 2)), dhalf);
+  const float dl = dhalf + __shfl_xor(dhalf, 32);
+  if (g == 0 && qrow < Sq) DLT[(size_t)bh * Sq + qrow] = dl;
 
   f32x16 adq[D / 32];  // dQ^T of this wave's 32 rows
 #pragma unroll
@@ -700,6 +743,16 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   }
 }
 
+template <int D>
+hipError_t launch_pre_bf16(const Problem& p, const void* o, const void* dout, float* dlt,
+                           hipStream_t stream) {
+  const long long rows = (long long)p.B * p.Hq * p.Sq;
+  const unsigned blocks = (unsigned)((2 * rows + THREADS - 1) / THREADS);
+  hipLaunchKernelGGL((bwd_pre_bf16_kernel<D>), dim3(blocks), dim3(THREADS), 0, stream,
+                     (const bf16*)o, (const bf16*)dout, dlt, rows);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_pre_t(const Problem& p, const void* o, const void* dout, float* dlt,
                         hipStream_t stream) {
@@ -742,13 +795,13 @@ hipError_t launch_dkdv_t(const Problem& p, const void* q, const void* k, const v
 
 template <int D, bool CAUSAL>
 hipError_t launch_dq_t(const Problem& p, const void* q, const void* k, const void* v,
-                       const float* lse, const float* dlt, const void* dout, void* dq,
+                       const void* o, const float* lse, float* dlt, const void* dout, void* dq,
                        hipStream_t stream) {
   const int n_qt = (p.Sq + DQ_BM - 1) / DQ_BM;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)p.B * p.Hq * n_qt)),
                      dim3(DQ_THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
-                     (const bf16*)dout, lse, dlt, (bf16*)dq, p.Hq, p.Hq / p.Hkv, p.Sq, p.Skv,
-                     p.scale, p.scale * MATTN_LOG2E, n_qt);
+                     (const bf16*)o, (const bf16*)dout, lse, dlt, (bf16*)dq, p.Hq, p.Hq / p.Hkv,
+                     p.Sq, p.Skv, p.scale, p.scale * MATTN_LOG2E, n_qt);
   return hipGetLastError();
 }
 
@@ -756,8 +809,10 @@ hipError_t launch_dq_t(const Problem& p, const void* q, const void* k, const voi
 
 hipError_t launch_bwd_preprocess(const Problem& p, bool bf16_io, const void* o, const void* dout,
                                  float* dlt, hipStream_t stream) {
-  return bf16_io ? launch_pre_t<bf16>(p, o, dout, dlt, stream)
-                 : launch_pre_t<float>(p, o, dout, dlt, stream);
+  if (bf16_io)
+    return p.D == 64 ? launch_pre_bf16<64>(p, o, dout, dlt, stream)
+                     : launch_pre_bf16<128>(p, o, dout, dlt, stream);
+  return launch_pre_t<float>(p, o, dout, dlt, stream);
 }
 
 hipError_t launch_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
@@ -771,13 +826,13 @@ hipError_t launch_dkdv_bf16(const Problem& p, const void* q, const void* k, cons
 }
 
 hipError_t launch_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
-                          const float* lse, const float* dlt, const void* dout, void* dq,
+                          const void* o, const float* lse, float* dlt, const void* dout, void* dq,
                           hipStream_t stream) {
   if (p.D == 64)
-    return p.causal ? launch_dq_t<64, true>(p, q, k, v, lse, dlt, dout, dq, stream)
-                    : launch_dq_t<64, false>(p, q, k, v, lse, dlt, dout, dq, stream);
-  return p.causal ? launch_dq_t<128, true>(p, q, k, v, lse, dlt, dout, dq, stream)
-                  : launch_dq_t<128, false>(p, q, k, v, lse, dlt, dout, dq, stream);
+    return p.causal ? launch_dq_t<64, true>(p, q, k, v, o, lse, dlt, dout, dq, stream)
+                    : launch_dq_t<64, false>(p, q, k, v, o, lse, dlt, dout, dq, stream);
+  return p.causal ? launch_dq_t<128, true>(p, q, k, v, o, lse, dlt, dout, dq, stream)
+                  : launch_dq_t<128, false>(p, q, k, v, o, lse, dlt, dout, dq, stream);
 }
 
 }  // namespace mattn

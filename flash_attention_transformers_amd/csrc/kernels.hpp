@@ -29,8 +29,10 @@ hipError_t launch_bwd_preprocess(const Problem& p, bool bf16_io, const void* o,
 hipError_t launch_dkdv_bf16(const Problem& p, const void* q, const void* k, const void* v,
                             const float* lse, const float* dlt, const void* dout, void* dk,
                             void* dv, float* part, hipStream_t stream);
+// dQ for bf16; also forms D = rowsum(dO * O) itself (bitwise the preprocess
+// kernel's value) and stores it into dlt for the dK/dV kernel.
 hipError_t launch_dq_bf16(const Problem& p, const void* q, const void* k, const void* v,
-                          const float* lse, const float* dlt, const void* dout, void* dq,
+                          const void* o, const float* lse, float* dlt, const void* dout, void* dq,
                           hipStream_t stream);
 
 hipError_t launch_fwd_f32(const Problem& p, const float* q, const float* k, const float* v,

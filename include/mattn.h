@@ -98,13 +98,16 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
 
 /* The stages mattn_bwd enqueues, selectable for callers that schedule or
  * time them separately.  Same arguments, checks and workspace as mattn_bwd;
- * `stages` is a non-zero OR of the flags below.  Stages must run in this
- * order (each reads what the one before wrote into `workspace` or the
- * outputs); calling mattn_bwd_stages with all three flags is exactly
- * mattn_bwd.  A stage not selected leaves its outputs untouched.
+ * `stages` is a non-zero OR of the flags below, and the selected stages run
+ * in the order listed.  Each reads what an earlier one wrote into
+ * `workspace` or the outputs, so separate calls follow the same order.
  *   MATTN_BWD_PREPROCESS  D = sum(dO * O) per query row into the workspace
- *   MATTN_BWD_DKDV        dK, dV (needs the preprocess result)
- *   MATTN_BWD_DQ          dQ     (needs the preprocess result) */
+ *   MATTN_BWD_DQ          dQ; for bf16 it also forms D itself and stores it
+ *                         (bitwise the preprocess value), so a bf16 caller
+ *                         may skip the preprocess; fp32 reads the stored D
+ *   MATTN_BWD_DKDV        dK, dV (reads the stored D)
+ * mattn_bwd enqueues DQ then DKDV for bf16, and all three for fp32; a caller
+ * that enqueues all three for bf16 gets the same bits. */
 enum { MATTN_BWD_PREPROCESS = 1, MATTN_BWD_DKDV = 2, MATTN_BWD_DQ = 4 };
 mattn_status mattn_bwd_stages(const void* q, const void* k, const void* v, const void* o,
                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
