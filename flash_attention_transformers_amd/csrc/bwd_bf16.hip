@@ -195,7 +195,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) char QT1[Copy::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) char QT2[Copy::BUF_BYTES];
   // P handed from each P-wave to its dS-wave, by step parity:
-  // [parity][slice][sub-block][lane][16 bf16].
+  // [parity][slice][sub-block][half][lane][8 bf16] (16 bytes per lane, so
+  // a wave's 16-byte accesses cover all banks once).
   constexpr int PEX_PAR = 4 * NSUB * 64 * 16;
   __shared__ __attribute__((aligned(16))) bf16 Pex[2 * PEX_PAR];
   auto QTbuf = [&](auto b) __attribute__((always_inline)) -> char* {
@@ -291,8 +292,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   SW sw;
   sw.init(lane);
-  // This lane's 32 bytes of the P hand-off for sub-block 0 of parity 0.
-  int pex_lane = (slice * NSUB * 64 + lane) * 16;
+  // This lane's first 16 bytes of the P hand-off, sub-block 0, parity 0.
+  int pex_lane = (slice * NSUB * 2 * 64 + lane) * 8;
   asm volatile("" : "+v"(pex_lane));
   // S = Q K^T (P-wave) or dP = dO V^T (dS-wave) for one tile: lane = key
   // column, registers = query rows; both sub-blocks as independent chains.
@@ -335,8 +336,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           pb[qb][i >> 3][i & 7] = (bf16)pr;
         }
       }
-      *reinterpret_cast<bf16x8*>(pex + qb * 64 * 16) = pb[qb][0];
-      *reinterpret_cast<bf16x8*>(pex + qb * 64 * 16 + 8) = pb[qb][1];
+      *reinterpret_cast<bf16x8*>(pex + (2 * qb) * 64 * 8) = pb[qb][0];
+      *reinterpret_cast<bf16x8*>(pex + (2 * qb + 1) * 64 * 8) = pb[qb][1];
     }
   };
   // dV^T += dO^T P.
@@ -366,8 +367,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      bf16x8 (&dsb)[NSUB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < NSUB; ++qb) {
-      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pex + qb * 64 * 16);
-      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pex + qb * 64 * 16 + 8);
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pex + (2 * qb) * 64 * 8);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pex + (2 * qb + 1) * 64 * 8);
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt[qb * 32 + 8 * blk + 4 * g]);
