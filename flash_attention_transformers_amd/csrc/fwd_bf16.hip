@@ -6,7 +6,9 @@
 // heads follow row T15 (query head h reads KV head h / G), here by index
 // arithmetic with no repeated K/V.
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one head):
+// Work decomposition (one workgroup = 4 waves = 128 query rows of one head,
+// or 8 waves = 256 rows of one head or 128 rows of each of two query heads
+// that read the same KV head):
 //  * each wave owns 32 query rows and keeps them as the B operand of
 //    S^T = K Q^T in registers for the whole kernel (lane = query column);
 //  * K/V tiles of 64 keys are copied straight from global memory into
@@ -34,31 +36,37 @@ namespace mattn {
 
 namespace {
 
-// Four waves per workgroup; each wave owns QB blocks of 32 query rows.  The
-// code is written for any QB, but QB = 1: two blocks per wave (one wave per
-// SIMD with up to 512 registers, each K/V fragment feeding two MFMAs) made
-// the register allocator spill heavily.
-template <int D>
+// WAVES waves per workgroup, each owning QB blocks of 32 query rows of one of
+// the workgroup's HPW query heads (HPW > 1 only for heads that share a KV
+// head, so that every wave reads the same K/V tiles).  The code is written
+// for any QB, but QB = 1: two blocks per wave (one wave per SIMD with up to
+// 512 registers, each K/V fragment feeding two MFMAs) made the register
+// allocator spill heavily.  Four waves run two workgroups per CU; eight run
+// one, which halves the K/V bytes copied into each CU's LDS per query row.
+template <int D, int WAVES_, int HPW_>
 struct FwdTile {
   static constexpr int QB = 1;
   static constexpr int BN = 64;       // keys per tile
   static constexpr int KB = BN / 32;  // 32-key blocks per tile
-  static constexpr int WAVES = 4;
+  static constexpr int WAVES = WAVES_;
+  static constexpr int HPW = HPW_;    // query heads per workgroup
   static constexpr int THREADS = 64 * WAVES;
-  static constexpr int BM = 32 * QB * WAVES;     // query rows per workgroup
+  static constexpr int WPH = WAVES / HPW;        // waves per query head
+  static constexpr int BM = 32 * QB * WPH;       // query rows per workgroup
+  static_assert(WAVES % HPW == 0, "waves per head");
   static constexpr int KP = RowPitch<D>::value;  // K tile: read as row operands
   static constexpr int VP = TrPitch<D>::value;   // V tile: read transposed
   using KTile = DirectTile<D, BN, KP, THREADS>;
   using VTile = DirectTile<D, BN, VP, THREADS>;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(FwdTile<D>::THREADS, FwdTile<D>::QB == 2 ? 1 : 2)
+template <int D, bool CAUSAL, int WAVES, int HPW>
+__global__ __launch_bounds__(64 * WAVES, WAVES == 4 ? 2 : 1)
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      const bf16* __restrict__ V, bf16* __restrict__ O,
                      float* __restrict__ LSE, int Hq, int G, int Sq, int Skv,
                      float c /* scale*log2(e) */, int n_qt) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, WAVES, HPW>;
   constexpr int QB = T::QB, KB = T::KB, FWD_BN = T::BN;
   // Double-buffered K and V tiles, filled straight from global memory.  Each
   // buffer is its own LDS object: the compiler tracks copies in flight per
@@ -79,17 +87,24 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
 
-  int bh, qt;
-  tile_of_block(blockIdx.x, gridDim.x / n_qt, n_qt, CAUSAL, bh, qt);
-  const int h = bh % Hq, b = bh / Hq;
+  // Workgroup -> (batch, group of HPW query heads, query tile); this wave's
+  // head within the group, and its rows within the tile.
+  int bg, qt;
+  tile_of_block(blockIdx.x, gridDim.x / n_qt, n_qt, CAUSAL, bg, qt);
+  const int hg = Hq / HPW;  // head groups per batch entry
+  const int b = bg / hg;
+  const int h0 = (bg - b * hg) * HPW;  // first head of the group
+  // Wave-uniform; readfirstlane keeps the Q descriptor in scalar registers.
+  const int h = __builtin_amdgcn_readfirstlane(h0 + wave / T::WPH);
+  const int bh = b * Hq + h;
   const int Hkv = Hq / G;
-  const size_t kv_off = ((size_t)(b * Hkv + h / G) * Skv) * D;
+  const size_t kv_off = ((size_t)(b * Hkv + h0 / G) * Skv) * D;
   const bf16* Kh = K + kv_off;
   const bf16* Vh = V + kv_off;
   const Buf qbuf(Q + (size_t)bh * Sq * D, (uint32_t)Sq * D * 2);
 
   const int q0 = qt * T::BM;
-  const int qw0 = q0 + wave * 32 * QB;     // first query of this wave
+  const int qw0 = q0 + (wave % T::WPH) * 32 * QB;  // first query of this wave
   const int diag = Skv - Sq;               // key j visible to query i iff j <= i + diag
   auto qrow_of = [&](int qb) { return qw0 + 32 * qb + l32; };  // this lane's queries
 
@@ -388,23 +403,46 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
 }  // namespace
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int WAVES, int HPW>
 static hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v,
                              void* o, float* lse, hipStream_t stream) {
-  const int n_qt = (p.Sq + FwdTile<D>::BM - 1) / FwdTile<D>::BM;
-  const long long blocks = (long long)p.B * p.Hq * n_qt;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(FwdTile<D>::THREADS), 0,
-                     stream, (const bf16*)q, (const bf16*)k, (const bf16*)v, (bf16*)o, lse, p.Hq,
-                     p.Hq / p.Hkv, p.Sq, p.Skv, p.scale * MATTN_LOG2E, n_qt);
+  using T = FwdTile<D, WAVES, HPW>;
+  const int n_qt = (p.Sq + T::BM - 1) / T::BM;
+  const long long blocks = (long long)p.B * (p.Hq / HPW) * n_qt;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, WAVES, HPW>), dim3((unsigned)blocks),
+                     dim3(T::THREADS), 0, stream, (const bf16*)q, (const bf16*)k, (const bf16*)v,
+                     (bf16*)o, lse, p.Hq, p.Hq / p.Hkv, p.Sq, p.Skv, p.scale * MATTN_LOG2E, n_qt);
   return hipGetLastError();
+}
+
+// Workgroup shape.  Eight waves (one workgroup per CU) copy half the K/V bytes
+// per query row into LDS, which pays once a workgroup walks many key tiles;
+// with grouped heads they take two query heads of one KV head (128 rows
+// each, so causal masking wastes no more than with four waves), otherwise
+// 256 rows of one head (causal rows then walk up to 224 fully masked keys,
+// so that shape is kept for non-causal attention).  Short key ranges and
+// small grids keep four waves and two workgroups per CU.
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_shape(const Problem& p, const void* q, const void* k, const void* v,
+                                   void* o, float* lse, hipStream_t stream) {
+  if constexpr (D == 128) {
+    const int G = p.Hq / p.Hkv;
+    const bool long_kv = p.Skv >= 2048;
+    if (long_kv && G % 2 == 0 && (long long)p.B * (p.Hq / 2) * ((p.Sq + 127) / 128) >= 512)
+      return launch_fwd<D, CAUSAL, 8, 2>(p, q, k, v, o, lse, stream);
+    if constexpr (!CAUSAL)
+      if (long_kv && (long long)p.B * p.Hq * ((p.Sq + 255) / 256) >= 512)
+        return launch_fwd<D, CAUSAL, 8, 1>(p, q, k, v, o, lse, stream);
+  }
+  return launch_fwd<D, CAUSAL, 4, 1>(p, q, k, v, o, lse, stream);
 }
 
 hipError_t launch_fwd_bf16(const Problem& p, const void* q, const void* k, const void* v,
                            void* o, float* lse, hipStream_t stream) {
-  if (p.D == 64) return p.causal ? launch_fwd<64, true>(p, q, k, v, o, lse, stream)
-                                 : launch_fwd<64, false>(p, q, k, v, o, lse, stream);
-  return p.causal ? launch_fwd<128, true>(p, q, k, v, o, lse, stream)
-                  : launch_fwd<128, false>(p, q, k, v, o, lse, stream);
+  if (p.D == 64) return p.causal ? launch_fwd_shape<64, true>(p, q, k, v, o, lse, stream)
+                                 : launch_fwd_shape<64, false>(p, q, k, v, o, lse, stream);
+  return p.causal ? launch_fwd_shape<128, true>(p, q, k, v, o, lse, stream)
+                  : launch_fwd_shape<128, false>(p, q, k, v, o, lse, stream);
 }
 
 }  // namespace mattn
