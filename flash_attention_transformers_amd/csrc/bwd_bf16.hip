@@ -8,8 +8,11 @@
 // done here in registers in ascending group order, with no atomics, so the
 // result is bitwise reproducible.
 //
-// Three kernels on one stream:
+// Kernels, on one stream:
 //  1. preprocess: Dlt[row] = sum_d dO[row,d] * O[row,d]            (HBM bound)
+//     The bf16 dQ kernel forms the same values itself (bit for bit) and
+//     stores them, so the bf16 backward runs dQ first and then dK/dV, with
+//     no preprocess launch.
 //  2. dK/dV: one workgroup per 128 keys of one KV head, 8 waves: four
 //     32-key slices, each served by a pair of waves with split roles so that
 //     each wave fits in half a SIMD's registers and two waves share a SIMD:
@@ -25,13 +28,12 @@
 //     in registers.  Shapes with few KV tiles (short cross-attention KV) split
 //     the query range into fixed chunks that write fp32 partials, summed
 //     afterwards in chunk order by a reduction kernel.
-//  3. dQ: one workgroup per 128 query rows, 8 waves: four 32-row slices,
-//     each served by two waves that take the two 32-key halves of every
-//     64-key tile.  A wave keeps its 32 rows of Q and dO in registers and
-//     walks the K/V tiles:
+//  3. dQ: each wave owns 32 query rows, keeps their Q and dO in registers
+//     and walks the 64-key K/V tiles of its head:
 //        S^T = K Q^T, dP^T = V dO^T        (lane = query column)
 //        dQ^T += K^T dS^T
-//     and the two key-half partials are summed in a fixed order at the end.
+//     One workgroup of 4 waves per 128 query rows of one head; two
+//     workgroups share a CU.
 // Q/dO and K/V tiles are staged in LDS once each, in a layout (SwzTile)
 // whose row reads and transposed reads are both free of bank conflicts;
 // every transposed MFMA operand (dO^T, Q^T, K^T) is read from that copy with

@@ -94,6 +94,13 @@ def test_parity_eight_wave_forward(w, dev):
     H.check_sampled(w, dev, [(0, 0), (0, w.Hkv - 1)], rows_per_head=rows, backward=False)
 
 
+# Backward on a long GQA shape (group size 2) with ragged lengths and the
+# causal diagonal off the tile grid.
+def test_parity_long_gqa_backward(dev):
+    w = wl("gqa2_causal_ragged_long", 1, 32, 16, 4000, 4100, 128, True)
+    H.check_sampled(w, dev, [(0, 0), (0, 15)])
+
+
 @pytest.mark.parametrize("name", ["dit_cross_512", "dit_cross_257"])
 def test_parity_dit_cross_workload(name, dev):
     H.check_sampled(W.WORKLOADS[name], dev, [(0, 0), (0, 9)])
