@@ -162,6 +162,63 @@ struct SwzTile {
   }
 };
 
+// Layout of a [rows x 128] bf16 tile in LDS (rows a multiple of 16) that is
+// read both as row operands and transposed and is filled by direct copies
+// that write data only, no padding.  Rows form groups of four, and each group
+// is one copy instruction's kilobyte (64 lanes x 16 bytes): row k lives in
+// group 4 (k >> 4) + (k & 3), at slot (k >> 2) & 3 of it, and the 16-byte
+// chunk c (columns 8c .. 8c+7) of a row at slot a sits at chunk position
+// c ^ a.  Groups sit GS = 1088 bytes apart, so the four groups of rows k, k+1,
+// k+2, k+3 start in four different 64-byte bank segments:
+//  * a transposed read's four rows of one lane group are those four rows, one
+//    per segment, and the XOR keeps the two lane groups of a pass apart;
+//  * a row read's sixteen rows fill the four slots of four groups: the group
+//    picks the segment and the slot XOR the 16-byte bank group within it.
+// Both reads are then free of bank conflicts, and a lane's address for any
+// k-step or d-block is one of two per-lane bases plus a compile-time offset.
+// Reads start at rows that are multiples of 16.
+struct GrpTile128 {
+  static constexpr int D = 128;
+  static constexpr int GS = 1088;  // bytes from one group to the next
+  static constexpr int bytes(int rows) { return rows / 4 * GS; }
+  // First tile row of group G (its slot-0 row).
+  static __device__ __forceinline__ int group_row(int G) { return 16 * (G >> 2) + (G & 3); }
+  // Byte offset, from the first row of its group, of the global chunk that
+  // lane L of a group's copy brings: slot L >> 4, position L & 15.
+  static __device__ __forceinline__ uint32_t copy_lane_off(int L) {
+    const int a = L >> 4;
+    return (uint32_t)(4 * a * D + 8 * ((L & 15) ^ a)) * 2;
+  }
+  int rbase[2];  // row operand, k-step parity e (bytes)
+  int tbase[2];  // transposed operand, rows 0..7 (h = 0) and 8..15 (h = 1) of a 16-row step
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+    const int G0 = 4 * (l32 >> 4) + (l32 & 3), a = (l32 >> 2) & 3;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) rbase[e] = G0 * GS + 256 * a + 16 * ((2 * e + g) ^ a);
+    const int j = lane >> 4, s = lane & 15;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int at = 2 * h + (j >> 1);
+      tbase[h] = (s >> 2) * GS + 256 * at + 16 * ((2 * (j & 1) + ((s >> 1) & 1)) ^ at) + 8 * (s & 1);
+    }
+    asm volatile("" : "+v"(rbase[0]), "+v"(rbase[1]), "+v"(tbase[0]), "+v"(tbase[1]));
+  }
+  // A operand rows row0 .. row0+31, columns 16st .. 16st+15 (as ld_row_operand).
+  __device__ __forceinline__ bf16x8 row(const bf16* tile, int row0, int st) const {
+    const char* p = reinterpret_cast<const char*>(tile) + (row0 >> 4) * 4 * GS + 64 * (st >> 1);
+    return *reinterpret_cast<const bf16x8*>(p + rbase[st & 1]);
+  }
+  // A operand rows = tile columns 32db .. 32db+31, k-slots = tile rows
+  // row0 .. row0+15 (as TransReader).
+  __device__ __forceinline__ bf16x8 trans(const bf16* tile, int row0, int db) const {
+    const char* p = reinterpret_cast<const char*>(tile) + (row0 >> 4) * 4 * GS + 64 * db;
+    const bf16x4_t lo = ds_read_tr((const lds_bf16x4*)(p + tbase[0]));
+    const bf16x4_t hi = ds_read_tr((const lds_bf16x4*)(p + tbase[1]));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ f32x16 zero_f32x16() {
@@ -259,6 +316,32 @@ struct DirectTile {
       if (SLOTS % NT == 0 || q0 < SLOTS)
         ld16_to_lds(src, off[r], lds + q0 * 8);
     }
+  }
+};
+
+// Direct copy of a ROWS-row tile into the GrpTile128 layout by CW waves:
+// wave w takes groups w, w + CW, w + 2 CW, ...  Every lane's global offset
+// is one register (the group's first row is a per-wave and per-round
+// constant: with CW a multiple of 4 each round moves 4 CW rows), and each
+// copy instruction writes one whole group, so no padding is written.
+template <int ROWS, int CW>
+struct GrpCopy {
+  static constexpr int GROUPS = ROWS / 4;
+  static constexpr int ROUNDS = GROUPS / CW;
+  static_assert(ROWS % 16 == 0 && CW % 4 == 0 && GROUPS % CW == 0, "whole rounds");
+  uint32_t voff;  // bytes from the tile's first row, round 0
+  int lds0;       // byte offset of this wave's round-0 group (wave-uniform)
+  __device__ __forceinline__ void init(int w, int lane) {
+    voff = GrpTile128::copy_lane_off(lane) + (uint32_t)GrpTile128::group_row(w) * 256u;
+    lds0 = w * GrpTile128::GS;
+  }
+  // src: a descriptor whose base is the tile's first row and whose range ends
+  // at the last valid row, so rows past it land as zeros.
+  __device__ __forceinline__ void load(const Buf& src, void* tile) const {
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r)
+      ld16_to_lds(src, voff + (uint32_t)(r * 4 * CW * 256),
+                  reinterpret_cast<char*>(tile) + lds0 + r * CW * GrpTile128::GS);
   }
 };
 

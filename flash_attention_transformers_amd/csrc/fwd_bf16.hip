@@ -54,10 +54,15 @@ struct FwdTile {
   static constexpr int WPH = WAVES / HPW;        // waves per query head
   static constexpr int BM = 32 * QB * WPH;       // query rows per workgroup
   static_assert(WAVES % HPW == 0, "waves per head");
+  // D = 128: K and V tiles in the GrpTile128 layout (copies write no
+  // padding); D = 64: padded row-major tiles.
+  static constexpr bool GRP = D == 128;
   static constexpr int KP = RowPitch<D>::value;  // K tile: read as row operands
   static constexpr int VP = TrPitch<D>::value;   // V tile: read transposed
   using KTile = DirectTile<D, BN, KP, THREADS>;
   using VTile = DirectTile<D, BN, VP, THREADS>;
+  static constexpr int K_ELEMS = GRP ? GrpTile128::bytes(BN) / 2 : KTile::LDS_ELEMS;
+  static constexpr int V_ELEMS = GRP ? GrpTile128::bytes(BN) / 2 : VTile::LDS_ELEMS;
 };
 
 template <int D, bool CAUSAL, int WAVES, int HPW>
@@ -71,10 +76,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // Double-buffered K and V tiles, filled straight from global memory.  Each
   // buffer is its own LDS object: the compiler tracks copies in flight per
   // object, so reading one buffer does not wait for copies into another.
-  __shared__ __attribute__((aligned(16))) bf16 Ks0[T::KTile::LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 Ks1[T::KTile::LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs0[T::VTile::LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 Vs1[T::VTile::LDS_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Ks0[T::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Ks1[T::K_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs0[T::V_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 Vs1[T::V_ELEMS];
   auto Ks = [&](auto parity) -> bf16* {
     if constexpr (decltype(parity)::value == 0) return Ks0; else return Ks1;
   };
@@ -138,8 +143,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 
   typename T::KTile kt_ld;
   typename T::VTile vt_ld;
-  kt_ld.init(tid);
-  vt_ld.init(tid);
+  GrpCopy<FWD_BN, WAVES> gcp;  // D = 128: one copy pattern serves K and V
+  if constexpr (T::GRP) {
+    gcp.init(__builtin_amdgcn_readfirstlane(wave), lane);
+  } else {
+    kt_ld.init(tid);
+    vt_ld.init(tid);
+  }
   // Tile t's descriptors start at its first row and end at Skv, so rows past
   // the end (and pad slots) read as zeros.
   // Tile t goes to buffer t & 1; callers pass that parity as a compile-time
@@ -148,12 +158,16 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // in flight to the other.
   auto issue_k = [&](int t, bf16* dst) {
     const int j0 = t * FWD_BN;
-    kt_ld.load(Buf(Kh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), dst, tid);
+    const Buf src(Kh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2);
+    if constexpr (T::GRP) gcp.load(src, dst); else kt_ld.load(src, dst, tid);
   };
   auto issue_v = [&](int t, bf16* dst) {
     const int j0 = t * FWD_BN;
-    vt_ld.load(Buf(Vh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2), dst, tid);
+    const Buf src(Vh + (size_t)j0 * D, (uint32_t)(Skv - j0) * D * 2);
+    if constexpr (T::GRP) gcp.load(src, dst); else vt_ld.load(src, dst, tid);
   };
+  GrpTile128 gt;  // D = 128 operand reads
+  if constexpr (T::GRP) gt.init(lane);
   // Whether some key of tile t is invisible to some query of this wave.
   auto tile_masked = [&](int t) {
     const int j0 = t * FWD_BN;
@@ -188,7 +202,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     for (int st = 0; st < D / 16; ++st)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 a = ld_row_operand(Kb, T::KP, kb * 32, 16 * st, lane);
+        bf16x8 a;
+        if constexpr (T::GRP) a = gt.row(Kb, kb * 32, st);
+        else a = ld_row_operand(Kb, T::KP, kb * 32, 16 * st, lane);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sc[qb][kb] = mfma32(a, qf[qb][st], sc[qb][kb]);
       }
@@ -246,7 +262,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   };
   // O^T += V^T P^T; each V^T fragment feeds QB MFMAs.
   TransReader vtr;
-  vtr.init(T::VP, lane);
+  if constexpr (!T::GRP) vtr.init(T::VP, lane);
   auto pv_tile = [&](const bf16* Vb) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -255,7 +271,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         bf16x8 a[D / 32];
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
-          a[db] = vtr(Vb, T::VP, kb * 32 + 16 * t, db * 32);
+          if constexpr (T::GRP) a[db] = gt.trans(Vb, kb * 32 + 16 * t, db);
+          else a[db] = vtr(Vb, T::VP, kb * 32 + 16 * t, db * 32);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
