@@ -125,6 +125,18 @@ constexpr int DKDV_THREADS = 512;  // 4 key slices x 2 roles
 // as in DqKvCopy), then the tile's BWD_BMQ log-sum-exp and Dlt values.  Rows
 // past Sq load as zeros: their P is then finite and their dO, dP, Dlt and dS
 // are zero, so they add nothing.
+// A query tile's LSE and Dlt values (64 each, 4 bytes per lane): wave 0
+// copies the LSE values, wave 1 the Dlt values; the other waves issue the
+// same copy with an empty descriptor into a sink, so that the copy is not
+// under a branch.
+__device__ __forceinline__ void dkdv_copy_stats(const Buf& lse, const Buf& dlt, char* buf, int w0,
+                                                int lane, int lse_off, int dlt_off, int sink_off) {
+  const bool w_lse = w0 == 0, w_dlt = w0 == 64;
+  Buf src = w_lse ? lse : dlt;
+  if (!w_lse && !w_dlt) src.r = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
+  ld4_to_lds(src, lane * 4, buf + (w_lse ? lse_off : w_dlt ? dlt_off : sink_off));
+}
+
 template <int D>
 struct DkdvCopy {
   static constexpr int P = SwzTile<D>::P;
@@ -159,13 +171,32 @@ struct DkdvCopy {
       const int q0 = r * DKDV_THREADS + w0;
       ld16_to_lds(q0 < TILE_SLOTS ? q : dout, off[r], buf + q0 * 16);
     }
-    // Wave 0 copies the LSE values, wave 1 the Dlt values; the other waves
-    // issue the same copy with an empty descriptor into a sink, so that the
-    // copy is not under a branch.
-    const bool w_lse = w0 == 0, w_dlt = w0 == 64;
-    Buf src = w_lse ? lse : dlt;
-    if (!w_lse && !w_dlt) src.r = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
-    ld4_to_lds(src, lane * 4, buf + (w_lse ? LSE_OFF : w_dlt ? DLT_OFF : SINK_OFF));
+    dkdv_copy_stats(lse, dlt, buf, w0, lane, LSE_OFF, DLT_OFF, SINK_OFF);
+  }
+};
+
+// D = 128: the Q and dO tiles in the GrpTile128 layout, two groups of four
+// rows per wave and tile (no padding written), then the same LSE and Dlt
+// copies.
+template <>
+struct DkdvCopy<128> {
+  static constexpr int TILE_ELEMS = GrpTile128::bytes(BWD_BMQ) / 2;  // bf16 per tensor
+  static constexpr int LSE_OFF = 2 * TILE_ELEMS * 2;                 // bytes
+  static constexpr int DLT_OFF = LSE_OFF + BWD_BMQ * 4;
+  static constexpr int SINK_OFF = DLT_OFF + BWD_BMQ * 4;
+  static constexpr int BUF_BYTES = SINK_OFF + BWD_BMQ * 4;
+  static_assert(BWD_BMQ == 64, "one 4-byte copy per lane for LSE and Dlt");
+  GrpCopy<BWD_BMQ, DKDV_THREADS / 64> g;
+  int w0;
+  __device__ __forceinline__ void init(int tid) {
+    w0 = __builtin_amdgcn_readfirstlane(tid & ~63);
+    g.init(w0 >> 6, tid & 63);
+  }
+  __device__ __forceinline__ void load(const Buf& q, const Buf& dout, const Buf& lse,
+                                       const Buf& dlt, char* buf, int lane) const {
+    g.load(q, buf);
+    g.load(dout, buf + TILE_ELEMS * 2);
+    dkdv_copy_stats(lse, dlt, buf, w0, lane, LSE_OFF, DLT_OFF, SINK_OFF);
   }
 };
 
@@ -191,7 +222,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                      int nsplit, int q_chunk) {
   constexpr int BMQ = BWD_BMQ;            // query rows per step (two 32-row sub-blocks)
   constexpr int NSUB = BMQ / 32;
-  using SW = SwzTile<D>;
+  using SW = std::conditional_t<D == 128, GrpTile128, SwzTile<D>>;
   using Copy = DkdvCopy<D>;
   __shared__ __attribute__((aligned(16))) char QT0[Copy::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) char QT1[Copy::BUF_BYTES];
@@ -569,6 +600,34 @@ struct DqKvCopy {
   }
 };
 
+// Tile layout and copy of the dQ kernel's [K | V] buffers: D = 128 uses the
+// GrpTile128 layout (each wave copies four groups of four rows per tensor,
+// no padding written); D = 64 the padded SwzTile layout.
+template <int D>
+struct DqLayout {
+  using SW = SwzTile<D>;
+  using Copy = DqKvCopy<D>;
+  static constexpr int VOFF = Copy::TILE_SLOTS * 8;  // V tile's offset in a buffer (elements)
+  static constexpr int BUF_ELEMS = Copy::BUF_ELEMS;
+  static_assert(SW::P * DQ_BN == VOFF, "V tile follows the K tile");
+};
+template <>
+struct DqLayout<128> {
+  using SW = GrpTile128;
+  static constexpr int VOFF = GrpTile128::bytes(DQ_BN) / 2;
+  static constexpr int BUF_ELEMS = 2 * VOFF;
+  struct Copy {
+    GrpCopy<DQ_BN, DQ_WAVES> g;
+    __device__ __forceinline__ void init(int tid) {
+      g.init(__builtin_amdgcn_readfirstlane(tid >> 6), tid & 63);
+    }
+    __device__ __forceinline__ void load(const Buf& k, const Buf& v, bf16* buf) const {
+      g.load(k, buf);
+      g.load(v, buf + VOFF);
+    }
+  };
+};
+
 // dQ_i = scale * sum_j dS_ij K_j for a block of DQ_BM query rows.  Each wave
 // keeps its 32 rows of Q and dO in registers and walks every 64-key tile in
 // two 32-key halves.  K/V tiles arrive by direct copies into two LDS
@@ -584,15 +643,14 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
                    const bf16* __restrict__ dO, const float* __restrict__ LSE,
                    float* __restrict__ DLT, bf16* __restrict__ dQ, int Hq, int G, int Sq,
                    int Skv, float scale, float c, int n_qt) {
-  using SW = SwzTile<D>;
-  using Copy = DqKvCopy<D>;
-  constexpr int VOFF = Copy::TILE_SLOTS * 8;  // V tile's offset in a buffer (elements)
-  __shared__ __attribute__((aligned(16))) bf16 KV0[Copy::BUF_ELEMS];
-  __shared__ __attribute__((aligned(16))) bf16 KV1[Copy::BUF_ELEMS];
+  using SW = typename DqLayout<D>::SW;
+  using Copy = typename DqLayout<D>::Copy;
+  constexpr int VOFF = DqLayout<D>::VOFF;  // V tile's offset in a buffer (elements)
+  __shared__ __attribute__((aligned(16))) bf16 KV0[DqLayout<D>::BUF_ELEMS];
+  __shared__ __attribute__((aligned(16))) bf16 KV1[DqLayout<D>::BUF_ELEMS];
   auto KVbuf = [&](auto b) __attribute__((always_inline)) -> bf16* {
     if constexpr (decltype(b)::value == 0) return KV0; else return KV1;
   };
-  static_assert(SW::P * DQ_BN == VOFF, "V tile follows the K tile");
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
