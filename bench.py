@@ -367,7 +367,7 @@ def main():
     f1.record(stream)
     torch.cuda.synchronize()
     fwd_ms = f0.elapsed_time(f1) / args.steps
-    bwd_ms = ms_step - fwd_ms
+    bwd_ms = ms_step - fwd_ms if w.backward else None
 
     fwd_flop = w.fwd_flop()
     step_flop = fwd_flop + (w.bwd_flop() if w.backward else 0.0)
@@ -407,7 +407,8 @@ def main():
         "data": "synthetic (seeded N(0,1), resident in HBM)",
         "config": {
             "workload": f"{w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} Sq={w.Sq} Skv={w.Skv} "
-                        f"D={w.D} causal={int(w.causal)}; step = forward + backward",
+                        f"D={w.D} causal={int(w.causal)}; step = "
+                        + ("forward + backward" if w.backward else "forward only"),
             "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * value / peak, 2),
@@ -416,7 +417,7 @@ def main():
         "bwd_tflops": None if bwd_tf is None else round(bwd_tf, 2),
         "bwd_pct_of_peak": None if bwd_tf is None else round(100 * bwd_tf / peak, 2),
         "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
+        "bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
         "kernel_ms_note": "per-kernel spans from a second pass of the same steps with an event "
                           "between kernels (about 12 us of event cost per kernel boundary)",
         "wall_s_timed_region": round(wall, 4),

@@ -15,6 +15,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "grp_layout.hpp"
+
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -162,46 +164,31 @@ struct SwzTile {
   }
 };
 
-// Layout of a [rows x 128] bf16 tile in LDS (rows a multiple of 16) that is
-// read both as row operands and transposed and is filled by direct copies
-// that write data only, no padding.  Rows form groups of four, and each group
-// is one copy instruction's kilobyte (64 lanes x 16 bytes): row k lives in
-// group 4 (k >> 4) + (k & 3), at slot (k >> 2) & 3 of it, and the 16-byte
-// chunk c (columns 8c .. 8c+7) of a row at slot a sits at chunk position
-// c ^ a.  Groups sit GS = 1088 bytes apart, so the four groups of rows k, k+1,
-// k+2, k+3 start in four different 64-byte bank segments:
+// The grouped layout of a [rows x 128] bf16 tile in LDS (rows a multiple of
+// 16; index arithmetic in grp_layout.hpp), read both as row operands and
+// transposed and filled by direct copies that write data only, no padding.
+// Rows form groups of four, each one copy instruction's kilobyte, and groups
+// sit 1088 bytes apart, so the four groups of rows k, k+1, k+2, k+3 start in
+// four different 64-byte bank segments:
 //  * a transposed read's four rows of one lane group are those four rows, one
-//    per segment, and the XOR keeps the two lane groups of a pass apart;
+//    per segment, and the chunk XOR (by slot) keeps the two lane groups of a
+//    pass apart;
 //  * a row read's sixteen rows fill the four slots of four groups: the group
-//    picks the segment and the slot XOR the 16-byte bank group within it.
+//    picks the segment and the XOR the 16-byte bank group within it.
 // Both reads are then free of bank conflicts, and a lane's address for any
 // k-step or d-block is one of two per-lane bases plus a compile-time offset.
 // Reads start at rows that are multiples of 16.
 struct GrpTile128 {
-  static constexpr int D = 128;
-  static constexpr int GS = 1088;  // bytes from one group to the next
+  static constexpr int D = grp::D;
+  static constexpr int GS = grp::GS;
   static constexpr int bytes(int rows) { return rows / 4 * GS; }
-  // First tile row of group G (its slot-0 row).
-  static __device__ __forceinline__ int group_row(int G) { return 16 * (G >> 2) + (G & 3); }
-  // Byte offset, from the first row of its group, of the global chunk that
-  // lane L of a group's copy brings: slot L >> 4, position L & 15.
-  static __device__ __forceinline__ uint32_t copy_lane_off(int L) {
-    const int a = L >> 4;
-    return (uint32_t)(4 * a * D + 8 * ((L & 15) ^ a)) * 2;
-  }
   int rbase[2];  // row operand, k-step parity e (bytes)
   int tbase[2];  // transposed operand, rows 0..7 (h = 0) and 8..15 (h = 1) of a 16-row step
   __device__ __forceinline__ void init(int lane) {
-    const int l32 = lane & 31, g = lane >> 5;
-    const int G0 = 4 * (l32 >> 4) + (l32 & 3), a = (l32 >> 2) & 3;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) rbase[e] = G0 * GS + 256 * a + 16 * ((2 * e + g) ^ a);
-    const int j = lane >> 4, s = lane & 15;
+    for (int e = 0; e < 2; ++e) rbase[e] = grp::row_base(lane, e);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int at = 2 * h + (j >> 1);
-      tbase[h] = (s >> 2) * GS + 256 * at + 16 * ((2 * (j & 1) + ((s >> 1) & 1)) ^ at) + 8 * (s & 1);
-    }
+    for (int h = 0; h < 2; ++h) tbase[h] = grp::trans_base(lane, h);
     asm volatile("" : "+v"(rbase[0]), "+v"(rbase[1]), "+v"(tbase[0]), "+v"(tbase[1]));
   }
   // A operand rows row0 .. row0+31, columns 16st .. 16st+15 (as ld_row_operand).
@@ -332,16 +319,16 @@ struct GrpCopy {
   uint32_t voff;  // bytes from the tile's first row, round 0
   int lds0;       // byte offset of this wave's round-0 group (wave-uniform)
   __device__ __forceinline__ void init(int w, int lane) {
-    voff = GrpTile128::copy_lane_off(lane) + (uint32_t)GrpTile128::group_row(w) * 256u;
-    lds0 = w * GrpTile128::GS;
+    voff = grp::copy_off(CW, w, lane, 0);
+    lds0 = grp::copy_dst(CW, w, 0);
   }
   // src: a descriptor whose base is the tile's first row and whose range ends
   // at the last valid row, so rows past it land as zeros.
   __device__ __forceinline__ void load(const Buf& src, void* tile) const {
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r)
-      ld16_to_lds(src, voff + (uint32_t)(r * 4 * CW * 256),
-                  reinterpret_cast<char*>(tile) + lds0 + r * CW * GrpTile128::GS);
+      ld16_to_lds(src, voff + (grp::copy_off(CW, 0, 0, r) - grp::copy_off(CW, 0, 0, 0)),
+                  reinterpret_cast<char*>(tile) + lds0 + (grp::copy_dst(CW, 0, r) - grp::copy_dst(CW, 0, 0)));
   }
 };
 
