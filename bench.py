@@ -78,7 +78,7 @@ def roofline_kernel(stage: str, dtype: str) -> str:
 def kernel_source_sha(kernel: str) -> str:
     csrc = os.path.join(ROOT, "flash_attention_transformers_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "common.hpp"):
+    for f in (KERNEL_SOURCES[kernel], "common.hpp", "grp_layout.hpp"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
