@@ -18,6 +18,7 @@ Prints ONE JSON line.  `value` is credited TFLOP/s of the whole step:
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
     python bench.py --copy-probe   # plain 1 GiB device copy, to calibrate HBM byte counters
+    python bench.py --gemm-probe   # library bf16 GEMM rate: what a plain contraction reaches here
 
 The roofline object describes the kernel with the largest share of the step.
 Algorithmic work per launch, with F = 4*B*Hq*Sq*Skv*D (halved when causal):
@@ -98,6 +99,33 @@ def copy_probe(steps: int):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe_bytes_per_launch": n, "launches": steps}), flush=True)
+
+
+def gemm_probe(steps: int):
+    """Rate of torch's bf16 matrix product (the vendor GEMM library) on square
+    operands: the rate a plain dense contraction reaches on this GPU at its
+    sustained clock, a practical reference beside the nominal MFMA peak."""
+    import torch
+
+    out = {}
+    for n in (8192, 16384):
+        g = torch.Generator(device="cuda:0").manual_seed(0)
+        a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+        b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16, generator=g)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[f"gemm_bf16_{n}_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+        del a, b, c
+    out["peak_tflops"] = BF16_PEAK_TFLOPS
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -280,9 +308,13 @@ def main():
     ap.add_argument("--workload", default="gqa_causal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-probe", action="store_true", help="run the HBM calibration copy")
+    ap.add_argument("--gemm-probe", action="store_true", help="time the library bf16 GEMM")
     args = ap.parse_args()
     if args.copy_probe:
         copy_probe(max(args.steps, 1))
+        return
+    if args.gemm_probe:
+        gemm_probe(max(args.steps, 1))
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
