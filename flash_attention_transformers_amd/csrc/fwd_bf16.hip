@@ -12,7 +12,9 @@
 //  * each wave owns 32 query rows and keeps them as the B operand of
 //    S^T = K Q^T in registers for the whole kernel (lane = query column);
 //  * K/V tiles of 64 keys are copied straight from global memory into
-//    double-buffered LDS (buffer_load ... lds), one barrier per tile; K rows
+//    double-buffered LDS (buffer_load ... lds), one barrier per tile, for
+//    head dim 128 in the grouped layout of grp_layout.hpp (each copy
+//    instruction writes four whole rows, no padding); K rows
 //    are the A operand of S^T, and the A operand of O^T = V^T P^T is read
 //    transposed straight from the V tile with ds_read_b64_tr_b16, in the key
 //    order that P^T carries out of the S^T accumulator;
