@@ -789,18 +789,14 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   if (kt < n_kt) tile(B0{}, std::true_type{}, kt);
   if (kt + 1 < n_kt) tile(B1{}, std::true_type{}, kt + 1);
 
-  if (qrow < Sq) {
-    bf16* prow = dQ + ((size_t)bh * Sq + qrow) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = db * 32 + r * 8 + g * 4;
-        uint2 w;
-        w.x = pack_bf16x2(adq[db][4 * r] * scale, adq[db][4 * r + 1] * scale);
-        w.y = pack_bf16x2(adq[db][4 * r + 2] * scale, adq[db][4 * r + 3] * scale);
-        *reinterpret_cast<uint2*>(prow + d) = w;
-      }
+  // dQ rows through LDS (store_rows_bf16), staged in the buffer the last
+  // tile did not use: every wave finished reading it before that tile's
+  // barrier, and no copy goes to it afterwards.
+  static_assert(DQ_WAVES * stage_rows_bytes<D>() <= DqLayout<D>::BUF_ELEMS * 2, "staging fits a buffer");
+  {
+    bf16* st = (n_kt & 1) ? KV1 : KV0;
+    char* stg = reinterpret_cast<char*>(st) + slice * stage_rows_bytes<D>();
+    store_rows_bf16<D>(adq, scale, stg, dQ + ((size_t)bh * Sq + qw0) * D, Sq - qw0, lane);
   }
 }
 

@@ -341,6 +341,43 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
 }
 
+// Bytes of LDS that store_rows_bf16 stages one wave's 32 rows in.
+template <int D>
+constexpr int stage_rows_bytes() { return 32 * (2 * D + 16); }
+
+// Store of a wave's 32 output rows held in the MFMA C layout (lane column
+// l32 = row; register i of block db = column 32db + 8(i/4) + 4g + i%4, with
+// g = lane >> 5), scaled by mul and rounded to bf16.  Written directly, every
+// store instruction would touch 32 rows at 16 bytes each; instead the rows
+// go through wave-private LDS (stg: stage_rows_bytes<D>() bytes, row pitch
+// 2D + 16) and come back so that each store instruction writes whole
+// consecutive rows, 64 lanes x 16 bytes.  Rows at or past rows_valid
+// (counted from the first) are not written.  The LDS writes and reads are
+// the same wave's, in program order, so no barrier is involved.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(const f32x16 (&acc)[D / 32], float mul, char* stg,
+                                                bf16* out, int rows_valid, int lane) {
+  constexpr int SP = 2 * D + 16;
+  const int l32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint2 w;
+      w.x = pack_bf16x2(acc[db][4 * r] * mul, acc[db][4 * r + 1] * mul);
+      w.y = pack_bf16x2(acc[db][4 * r + 2] * mul, acc[db][4 * r + 3] * mul);
+      *reinterpret_cast<uint2*>(stg + l32 * SP + (db * 32 + r * 8 + g * 4) * 2) = w;
+    }
+  constexpr int CPR = D / 8;     // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = i * RPI + lane / CPR, ch = lane % CPR;
+    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * SP + ch * 16);
+    if (row < rows_valid) *reinterpret_cast<uint4*>(out + (size_t)row * D + ch * 8) = v;
+  }
+}
+
 // Workgroup -> (head, query tile) order, assuming round-robin dispatch of
 // consecutive workgroup ids over the 8 XCDs (id % 8 = XCD), each with its own
 // L2.  Non-causal: head-major, remapped so that each XCD walks a contiguous
