@@ -485,21 +485,16 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
   }
 
-  if (key >= Skv) return;
   const float mul = pwave ? 1.f : scale;  // dK = scale * Q^T dS
   if (nsplit == 1) {
-    bf16* pout = (pwave ? dV : dK) + kv_off + (size_t)key * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = db * 32 + r * 8 + g * 4;
-        uint2 w;
-        w.x = pack_bf16x2(acc[db][4 * r] * mul, acc[db][4 * r + 1] * mul);
-        w.y = pack_bf16x2(acc[db][4 * r + 2] * mul, acc[db][4 * r + 3] * mul);
-        *reinterpret_cast<uint2*>(pout + d) = w;
-      }
+    // dV (P-waves) and dK (dS-waves) rows through LDS (store_rows_bf16),
+    // staged in two query-tile buffers once every wave is past the walk.
+    static_assert(4 * stage_rows_bytes<D>() <= Copy::BUF_BYTES, "staging fits a buffer");
+    __syncthreads();
+    char* stg = (pwave ? QT0 : QT1) + slice * stage_rows_bytes<D>();
+    store_rows_bf16<D>(acc, mul, stg, (pwave ? dV : dK) + kv_off + (size_t)kw0 * D, Skv - kw0, lane);
   } else {
+    if (key >= Skv) return;
     // fp32 partials, unscaled: [dK, dV][nsplit][B*Hkv][n_kt*BWD_BN][D]
     const size_t rows_all = (size_t)(gridDim.x / nsplit / n_kt) * n_kt * BWD_BN;
     const size_t half = (size_t)nsplit * rows_all * D;

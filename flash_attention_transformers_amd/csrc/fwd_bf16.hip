@@ -397,26 +397,23 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     last_step(Even{}, sa);
   }
 
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = qrow_of(qb);
-    const float lt = l[qb] + __shfl_xor(l[qb], 32);
-    if (qrow < Sq) {
-      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-      bf16* orow = O + ((size_t)bh * Sq + qrow) * D;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int d = db * 32 + r * 8 + g * 4;
-          uint2 w;
-          w.x = pack_bf16x2(acc[qb][db][4 * r + 0] * inv, acc[qb][db][4 * r + 1] * inv);
-          w.y = pack_bf16x2(acc[qb][db][4 * r + 2] * inv, acc[qb][db][4 * r + 3] * inv);
-          *reinterpret_cast<uint2*>(orow + d) = w;
-        }
-      if (g == 0)
-        LSE[(size_t)bh * Sq + qrow] = lt > 0.f ? (m[qb] + log2f(lt)) * MATTN_LN2 : -MATTN_INF;
-    }
+  // O rows through LDS (store_rows_bf16), staged two waves per tile buffer
+  // once every wave is past the last tile's reads (four buffers serve eight
+  // waves).
+  static_assert(QB == 1, "one 32-row block per wave");
+  static_assert(2 * stage_rows_bytes<D>() <= 2 * (T::K_ELEMS < T::V_ELEMS ? T::K_ELEMS : T::V_ELEMS),
+                "two waves' staging fits a tile buffer");
+  __syncthreads();
+  {
+    const int sw = wave >> 1;
+    bf16* sbuf = sw == 0 ? Ks0 : sw == 1 ? Ks1 : sw == 2 ? Vs0 : Vs1;
+    char* stg = reinterpret_cast<char*>(sbuf) + (wave & 1) * stage_rows_bytes<D>();
+    const float lt = l[0] + __shfl_xor(l[0], 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    store_rows_bf16<D>(acc[0], inv, stg, O + ((size_t)bh * Sq + qw0) * D, Sq - qw0, lane);
+    const int qrow = qrow_of(0);
+    if (g == 0 && qrow < Sq)
+      LSE[(size_t)bh * Sq + qrow] = lt > 0.f ? (m[0] + log2f(lt)) * MATTN_LN2 : -MATTN_INF;
   }
 }
 
