@@ -343,22 +343,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 
 // Bytes of LDS that store_rows_bf16 stages one wave's 32 rows in.
 template <int D>
-constexpr int stage_rows_bytes() { return 32 * (2 * D + 16); }
+constexpr int stage_rows_bytes() { return stage::bytes(D); }
 
 // Store of a wave's 32 output rows held in the MFMA C layout (lane column
 // l32 = row; register i of block db = column 32db + 8(i/4) + 4g + i%4, with
 // g = lane >> 5), scaled by mul and rounded to bf16.  Written directly, every
 // store instruction would touch 32 rows at 16 bytes each; instead the rows
-// go through wave-private LDS (stg: stage_rows_bytes<D>() bytes, row pitch
-// 2D + 16) and come back so that each store instruction writes whole
-// consecutive rows, 64 lanes x 16 bytes.  Rows at or past rows_valid
-// (counted from the first) are not written.  The LDS writes and reads are
-// the same wave's, in program order, so no barrier is involved.
+// go through wave-private LDS (stg: stage_rows_bytes<D>() bytes; layout and
+// offsets in grp_layout.hpp, namespace stage) and come back so that each
+// store instruction writes whole consecutive rows, 64 lanes x 16 bytes.
+// Rows at or past rows_valid (counted from the first) are not written.  The
+// LDS writes and reads are the same wave's, in program order, so no barrier
+// is involved.  Rows 16-31 are staged with the 8-byte halves of each chunk
+// swapped (a half-wave's 8-byte writes to rows r and r+16 would otherwise
+// share banks); their read-back swaps them again.
 template <int D>
 __device__ __forceinline__ void store_rows_bf16(const f32x16 (&acc)[D / 32], float mul, char* stg,
                                                 bf16* out, int rows_valid, int lane) {
-  constexpr int SP = 2 * D + 16;
-  const int l32 = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
@@ -366,14 +367,14 @@ __device__ __forceinline__ void store_rows_bf16(const f32x16 (&acc)[D / 32], flo
       uint2 w;
       w.x = pack_bf16x2(acc[db][4 * r] * mul, acc[db][4 * r + 1] * mul);
       w.y = pack_bf16x2(acc[db][4 * r + 2] * mul, acc[db][4 * r + 3] * mul);
-      *reinterpret_cast<uint2*>(stg + l32 * SP + (db * 32 + r * 8 + g * 4) * 2) = w;
+      *reinterpret_cast<uint2*>(stg + stage::write_off(D, lane, db, r)) = w;
     }
-  constexpr int CPR = D / 8;     // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  static_assert(16 % (64 / (D / 8)) == 0, "an instruction's rows lie on one side of row 16");
 #pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int row = i * RPI + lane / CPR, ch = lane % CPR;
-    const uint4 v = *reinterpret_cast<const uint4*>(stg + row * SP + ch * 16);
+  for (int i = 0; i < 32 / (64 / (D / 8)); ++i) {
+    const int row = stage::read_row(D, i, lane), ch = stage::read_chunk(D, lane);
+    uint4 v = *reinterpret_cast<const uint4*>(stg + stage::read_off(D, i, lane));
+    if (stage::read_swapped(D, i)) v = make_uint4(v.z, v.w, v.x, v.y);
     if (row < rows_valid) *reinterpret_cast<uint4*>(out + (size_t)row * D + ch * 8) = v;
   }
 }

@@ -72,4 +72,24 @@ MATTN_HD constexpr int trans_addr(int lane, int row0, int db, int h) {
 }
 
 }  // namespace grp
+
+// Output staging (store_rows_bf16 in common.hpp): one wave's 32 rows of
+// head dim d bf16 in LDS at row pitch 2d + 16 bytes.  Lane (l32 = lane & 31,
+// g = lane >> 5) writes its 8 bytes of columns 32 db + 8 r + 4 g .. +3 of row
+// l32; rows 16-31 keep the two 8-byte halves of each 16-byte chunk swapped.
+namespace stage {
+MATTN_HD constexpr int pitch(int d) { return 2 * d + 16; }
+MATTN_HD constexpr int bytes(int d) { return 32 * pitch(d); }
+MATTN_HD constexpr int write_off(int d, int lane, int db, int r) {
+  return (lane & 31) * pitch(d) + (db * 32 + r * 8) * 2 + 8 * ((lane >> 5) ^ ((lane & 31) >> 4));
+}
+// Read-back: store instruction i, lane -> row and 16-byte chunk; rows of one
+// instruction lie on one side of row 16 (swapped halves iff row >= 16).
+MATTN_HD constexpr int read_row(int d, int i, int lane) { return i * (64 / (d / 8)) + lane / (d / 8); }
+MATTN_HD constexpr int read_chunk(int d, int lane) { return lane % (d / 8); }
+MATTN_HD constexpr int read_off(int d, int i, int lane) {
+  return read_row(d, i, lane) * pitch(d) + 16 * read_chunk(d, lane);
+}
+MATTN_HD constexpr bool read_swapped(int d, int i) { return i * (64 / (d / 8)) >= 16; }
+}  // namespace stage
 }  // namespace mattn

@@ -1,9 +1,10 @@
-// Host check of the grouped LDS tile layout (grp_layout.hpp): the direct
+// Host check of the LDS layouts in grp_layout.hpp.  Grouped tile: the direct
 // copies place every element of a 64 x 128 bf16 tile exactly once, the row
 // and transposed operand addresses find the elements the MFMA operands need,
 // and neither read pattern has bank conflicts (64 banks of 4 bytes; a row
 // read serves 16 lanes x 16 bytes per pass, a transposed read 32 lanes x
-// 8 bytes).  Prints "ok" and exits 0 on success.
+// 8 bytes).  Output staging: placement, read-back and conflict-free writes.
+// Prints "ok" and exits 0 on success.
 #include <cstdio>
 #include <cstdlib>
 #include <map>
@@ -83,6 +84,35 @@ int main() {
         }
         CHECK(bank_worst(addr, 32, 8) == 1, "transposed read bank conflict row0=%d db=%d h=%d", row0, db, h);
       }
+  // Output staging: every (row, column) of a wave's 32 rows written once,
+  // read back into the right place, half-wave 8-byte writes conflict free.
+  for (int d : {64, 128}) {
+    std::vector<int> st(mattn::stage::bytes(d), -1);
+    for (int db = 0; db < d / 32; ++db)
+      for (int r = 0; r < 4; ++r) {
+        std::vector<int> addr(64);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int a = mattn::stage::write_off(d, lane, db, r);
+          addr[lane] = a;
+          CHECK(a >= 0 && a + 8 <= mattn::stage::bytes(d) && a % 8 == 0, "staging write out of range");
+          for (int e = 0; e < 4; ++e) {
+            CHECK(st[a + 2 * e] == -1, "staging byte written twice");
+            st[a + 2 * e] = (lane & 31) * d + db * 32 + r * 8 + 4 * (lane >> 5) + e;
+          }
+        }
+        CHECK(bank_worst(addr, 32, 8) == 1, "staging write bank conflict d=%d db=%d r=%d", d, db, r);
+      }
+    for (int i = 0; i < 32 / (64 / (d / 8)); ++i)
+      for (int lane = 0; lane < 64; ++lane) {
+        const int a = mattn::stage::read_off(d, i, lane);
+        CHECK(a % 16 == 0, "staging read misaligned");
+        const int row = mattn::stage::read_row(d, i, lane), ch = mattn::stage::read_chunk(d, lane);
+        for (int e = 0; e < 8; ++e) {
+          const int src = mattn::stage::read_swapped(d, i) ? (e + 4) % 8 : e;
+          CHECK(st[a + 2 * src] == row * d + 8 * ch + e, "staging read-back d=%d i=%d lane=%d", d, i, lane);
+        }
+      }
+  }
   if (fails) {
     std::printf("%d failures\n", fails);
     return 1;
