@@ -23,9 +23,9 @@
 //     (lane = key column; K or V of the slice stays in registers as the MFMA
 //     B operand).  The dS-wave runs one query tile behind the P-wave, so the
 //     VALU work of one wave meets MFMA work of the other on their shared SIMD;
-//     Q/dO tiles are double-buffered in LDS.  The walk covers every query
-//     tile of every query head of the group, in ascending head order, summing
-//     in registers.  Shapes with few KV tiles (short cross-attention KV) split
+//     Q/dO tiles arrive two steps ahead in three LDS buffers.  The walk
+//     covers every query tile of every query head of the group, in ascending
+//     head order, summing in registers.  Shapes with few KV tiles (short cross-attention KV) split
 //     the query range into fixed chunks that write fp32 partials, summed
 //     afterwards in chunk order by a reduction kernel.
 //  3. dQ: each wave owns 32 query rows, keeps their Q and dO in registers
