@@ -126,15 +126,12 @@ constexpr int DKDV_THREADS = 512;  // 4 key slices x 2 roles
 // past Sq load as zeros: their P is then finite and their dO, dP, Dlt and dS
 // are zero, so they add nothing.
 // A query tile's LSE and Dlt values (64 each, 4 bytes per lane): wave 0
-// copies the LSE values, wave 1 the Dlt values; the other waves issue the
-// same copy with an empty descriptor into a sink, so that the copy is not
-// under a branch.
+// copies the LSE values, wave 1 the Dlt values (w0 is wave-uniform, and each
+// branch names its destination, so the copies keep their LDS alias scope).
 __device__ __forceinline__ void dkdv_copy_stats(const Buf& lse, const Buf& dlt, char* buf, int w0,
-                                                int lane, int lse_off, int dlt_off, int sink_off) {
-  const bool w_lse = w0 == 0, w_dlt = w0 == 64;
-  Buf src = w_lse ? lse : dlt;
-  if (!w_lse && !w_dlt) src.r = __builtin_amdgcn_make_buffer_rsrc(nullptr, (short)0, 0, 0x00020000);
-  ld4_to_lds(src, lane * 4, buf + (w_lse ? lse_off : w_dlt ? dlt_off : sink_off));
+                                                int lane, int lse_off, int dlt_off) {
+  if (w0 == 0) ld4_to_lds(lse, lane * 4, buf + lse_off);
+  else if (w0 == 64) ld4_to_lds(dlt, lane * 4, buf + dlt_off);
 }
 
 template <int D>
@@ -146,8 +143,7 @@ struct DkdvCopy {
   static constexpr int TILE_ELEMS = TILE_SLOTS * 8;             // bf16 per tensor
   static constexpr int LSE_OFF = 2 * TILE_SLOTS * 16;           // bytes
   static constexpr int DLT_OFF = LSE_OFF + BWD_BMQ * 4;
-  static constexpr int SINK_OFF = DLT_OFF + BWD_BMQ * 4;         // zeros from the other waves
-  static constexpr int BUF_BYTES = SINK_OFF + BWD_BMQ * 4;
+  static constexpr int BUF_BYTES = DLT_OFF + BWD_BMQ * 4;
   static_assert(2 * TILE_SLOTS % DKDV_THREADS == 0 && TILE_SLOTS % 64 == 0, "whole rounds");
   static_assert(BWD_BMQ == 64, "one 4-byte copy per lane for LSE and Dlt");
   uint32_t off[ROUNDS];
@@ -171,7 +167,7 @@ struct DkdvCopy {
       const int q0 = r * DKDV_THREADS + w0;
       ld16_to_lds(q0 < TILE_SLOTS ? q : dout, off[r], buf + q0 * 16);
     }
-    dkdv_copy_stats(lse, dlt, buf, w0, lane, LSE_OFF, DLT_OFF, SINK_OFF);
+    dkdv_copy_stats(lse, dlt, buf, w0, lane, LSE_OFF, DLT_OFF);
   }
 };
 
@@ -183,8 +179,7 @@ struct DkdvCopy<128> {
   static constexpr int TILE_ELEMS = GrpTile128::bytes(BWD_BMQ) / 2;  // bf16 per tensor
   static constexpr int LSE_OFF = 2 * TILE_ELEMS * 2;                 // bytes
   static constexpr int DLT_OFF = LSE_OFF + BWD_BMQ * 4;
-  static constexpr int SINK_OFF = DLT_OFF + BWD_BMQ * 4;
-  static constexpr int BUF_BYTES = SINK_OFF + BWD_BMQ * 4;
+  static constexpr int BUF_BYTES = DLT_OFF + BWD_BMQ * 4;
   static_assert(BWD_BMQ == 64, "one 4-byte copy per lane for LSE and Dlt");
   GrpCopy<BWD_BMQ, DKDV_THREADS / 64> g;
   int w0;
@@ -196,7 +191,7 @@ struct DkdvCopy<128> {
                                        const Buf& dlt, char* buf, int lane) const {
     g.load(q, buf);
     g.load(dout, buf + TILE_ELEMS * 2);
-    dkdv_copy_stats(lse, dlt, buf, w0, lane, LSE_OFF, DLT_OFF, SINK_OFF);
+    dkdv_copy_stats(lse, dlt, buf, w0, lane, LSE_OFF, DLT_OFF);
   }
 };
 
