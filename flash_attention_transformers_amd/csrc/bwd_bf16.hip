@@ -455,11 +455,16 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     }
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     __syncthreads();
-    if (it + 2 < n_it) issue(it + 2, prev);
-    if (pwave)
+    // Tile it+2's copies: the P-waves issue theirs after the dV MFMAs, the
+    // dS-waves before their dS arithmetic, so that the copies do not all
+    // start at the barrier beside the operand reads of both roles.
+    if (pwave) {
       dv_tile(dOs(cur));
-    else
+      if (it + 2 < n_it) issue(it + 2, prev);
+    } else {
+      if (it + 2 < n_it) issue(it + 2, prev);
       ds_tile(dlt_s(cur), pex, sc, dsb);
+    }
   };
 
   if (n_it > 0) __syncthreads();  // tiles 0 and 1 landed everywhere (waited for above)
