@@ -46,3 +46,17 @@ def test_bench_roofline_kernels_have_sources():
         for stage in ("fwd", "dkdv", "dq"):
             assert bench.roofline_kernel(stage, dtype) in bench.KERNEL_SOURCES
     assert bench.roofline_kernel("fwd", "bf16") == "fwd_bf16_kernel"
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asking for more exits with a message, before
+    touching any GPU."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
