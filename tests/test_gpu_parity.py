@@ -104,3 +104,33 @@ def test_parity_long_gqa_backward(dev):
 @pytest.mark.parametrize("name", ["dit_cross_512", "dit_cross_257"])
 def test_parity_dit_cross_workload(name, dev):
     H.check_sampled(W.WORKLOADS[name], dev, [(0, 0), (0, 9)])
+
+
+def _random_shapes(n, seed):
+    """Seeded small shapes spanning the parameter space: batch, group size,
+    head dim, ragged and one-row/one-key lengths, causal (Skv >= Sq) or not,
+    bf16 mostly and some fp32."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        G = int(rng.choice([1, 2, 4]))
+        Hkv = int(rng.integers(1, 4))
+        D = int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        Sq = int(rng.choice([1, int(rng.integers(2, 70)), int(rng.integers(70, 400))]))
+        Skv = int(rng.choice([1, int(rng.integers(2, 70)), int(rng.integers(70, 400))]))
+        if causal and Skv < Sq:
+            Sq, Skv = Skv, Sq
+        dtype = "f32" if i % 6 == 5 else "bf16"
+        out.append(wl(f"rand{i}_G{G}_D{D}_{'c' if causal else 'n'}_{Sq}x{Skv}_{dtype}",
+                      int(rng.integers(1, 3)), Hkv * G, Hkv, Sq, Skv, D, causal,
+                      dtype=dtype, seed=100 + i))
+    return out
+
+
+RANDOM = _random_shapes(24, 20261202)
+
+
+@pytest.mark.parametrize("w", RANDOM, ids=[w.name for w in RANDOM])
+def test_parity_random_shapes(w, dev):
+    H.check_full(w, dev)
