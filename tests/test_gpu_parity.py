@@ -134,3 +134,50 @@ RANDOM = _random_shapes(24, 20261202)
 @pytest.mark.parametrize("w", RANDOM, ids=[w.name for w in RANDOM])
 def test_parity_random_shapes(w, dev):
     H.check_full(w, dev)
+
+
+def test_parity_max_query_rows(dev):
+    """The longest query range the boundary accepts for one head at D = 128
+    (a tensor of 2^31 - 128 elements, so byte offsets inside the head reach
+    2^32 - 256), forward and backward.  Inputs are drawn on the GPU from a
+    seeded torch generator (N(0,1), rounded to bf16); rows at the start and
+    at the very end are compared with the oracle: O, LSE and dQ (each row's
+    dQ depends only on its own row and on K/V when attention is
+    non-causal).  dK/dV sum over all rows and are not compared here."""
+    import torch
+
+    import flash_attention_transformers_amd as fa
+
+    D, Skv = 128, 100
+    Sq = (1 << 31) // D - 1
+    gen = torch.Generator(device=dev).manual_seed(31)
+
+    def draw(n):
+        return torch.randn(1, 1, n, D, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+
+    q, k, v, do = draw(Sq), draw(Skv), draw(Skv), draw(Sq)
+    scale = D ** -0.5
+    o, lse = fa.fwd(q, k, v, causal=False, scale=scale)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=False, scale=scale)
+    torch.cuda.synchronize()
+    rows = torch.tensor(list(range(0, 64)) + list(range(Sq - 200, Sq)), device=dev)
+
+    def pick(t):
+        return t[0, 0].index_select(0, rows).float().cpu().numpy().astype(np.float64)
+
+    qs, dos, go, gdq = pick(q), pick(do), pick(o), pick(dq)
+    glse = lse[0, 0].index_select(0, rows).cpu().numpy().astype(np.float64)
+    kk = k[0, 0].float().cpu().numpy().astype(np.float64)
+    vv = v[0, 0].float().cpu().numpy().astype(np.float64)
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+    ro, rlse = H.oracle.forward_head(qs, kk, vv, False, scale)
+    rdq, _, _, _ = H.oracle.backward_head(qs, kk, vv, dos, False, scale)
+    tol = H.TOL["bf16"]
+    res = dict(o_max_abs=H.max_abs(go, ro), o_rel_l2=H.rel_l2(go, ro),
+               lse_max_abs=H.max_abs(glse, rlse), dq=H.rel_l2(gdq, rdq))
+    H.say(f"[parity max rows] Sq={Sq} {res}")
+    assert res["o_max_abs"] <= tol["o_max_abs"], res
+    assert res["o_rel_l2"] <= tol["o_rel_l2"], res
+    assert res["lse_max_abs"] <= tol["lse_max_abs"], res
+    assert res["dq"] <= tol["grad_rel_l2"], res
