@@ -120,24 +120,6 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   // (exact in bf16) and a zero scale zeroes it (every visible score is then
   // 0, whatever the multiplier).
   bf16x8 qf[QB][D / 16];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf[qb][s] = as_bf16x8(qbuf.ld16((uint32_t)(qrow_of(qb) * D + 16 * s + 8 * g) * 2));
-  if (!(c > 0.f)) {
-    const uint32_t flip = c < 0.f ? 0x80008000u : 0u, keep = c < 0.f ? ~0u : 0u;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
-        uint4 u = __builtin_bit_cast(uint4, qf[qb][s]);
-        u.x = (u.x & keep) ^ flip; u.y = (u.y & keep) ^ flip;
-        u.z = (u.z & keep) ^ flip; u.w = (u.w & keep) ^ flip;
-        qf[qb][s] = as_bf16x8(u);
-      }
-    c = c < 0.f ? -c : 1.f;
-  }
 
   int kv_end = Skv;
   if (CAUSAL) kv_end = min(Skv, q0 + T::BM + diag);
@@ -374,6 +356,26 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   issue_k(0, Ks(Even{}));
   if (n_kt > 1) issue_k(1, Ks(Odd{}));
   issue_v(0, Vs(Even{}));
+  // Q after the first copies: the tile copies then do not queue behind the
+  // Q loads (each of which touches 32 rows).
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      qf[qb][s] = as_bf16x8(qbuf.ld16((uint32_t)(qrow_of(qb) * D + 16 * s + 8 * g) * 2));
+  if (!(c > 0.f)) {
+    const uint32_t flip = c < 0.f ? 0x80008000u : 0u, keep = c < 0.f ? ~0u : 0u;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int s = 0; s < D / 16; ++s) {
+        uint4 u = __builtin_bit_cast(uint4, qf[qb][s]);
+        u.x = (u.x & keep) ^ flip; u.y = (u.y & keep) ^ flip;
+        u.z = (u.z & keep) ^ flip; u.w = (u.w & keep) ^ flip;
+        qf[qb][s] = as_bf16x8(u);
+      }
+    c = c < 0.f ? -c : 1.f;
+  }
   __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
   s_tile(Ks(Even{}), sa);
