@@ -317,7 +317,7 @@ def main():
         gemm_probe(max(args.steps, 1))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(attention heads shard across GPUs with no change to the kernel).", file=sys.stderr)
         sys.exit(2)
 

@@ -11,7 +11,7 @@ Recipe (the same for every workload):
 * Optional per-tensor multipliers (the DiT self-attention workload scales q
   and k by float32(1/sqrt(2)) *before* rounding).
 * For bf16 workloads every tensor is rounded to bfloat16 with
-  round-to-nearest-even; the checker receives exactly those rounded values
+  round-to-nearest-even; the oracle receives exactly those rounded values
   upcast to float64, so input rounding is never counted as kernel error.
 
 The shapes follow the decoder-training and DiT/world-model workloads of the
