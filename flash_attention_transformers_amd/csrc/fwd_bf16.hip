@@ -436,16 +436,21 @@ static hipError_t launch_fwd(const Problem& p, const void* q, const void* k, con
 // Workgroup shape.  Eight waves (one workgroup per CU) copy half the K/V bytes
 // per query row into LDS, which pays once a workgroup walks many key tiles;
 // with grouped heads they take two query heads of one KV head (128 rows
-// each, so causal masking wastes no more than with four waves), otherwise
-// 256 rows of one head (causal rows then walk up to 224 fully masked keys,
-// so that shape is kept for non-causal attention).  Short key ranges and
-// small grids keep four waves and two workgroups per CU.
+// each, so causal masking wastes no more than with four waves), or, causal
+// with groups of four or more, four heads of 64 rows each (less masked work
+// on the diagonal and twice as many, shorter, causal workgroups to balance
+// the CUs); otherwise 256 rows of one head (causal rows then walk up to 224
+// fully masked keys, so that shape is kept for non-causal attention).  Short
+// key ranges and small grids keep four waves and two workgroups per CU.
 template <int D, bool CAUSAL>
 static hipError_t launch_fwd_shape(const Problem& p, const void* q, const void* k, const void* v,
                                    void* o, float* lse, hipStream_t stream) {
   if constexpr (D == 128) {
     const int G = p.Hq / p.Hkv;
     const bool long_kv = p.Skv >= 2048;
+    if constexpr (CAUSAL)
+      if (long_kv && G % 4 == 0 && (long long)p.B * (p.Hq / 4) * ((p.Sq + 63) / 64) >= 512)
+        return launch_fwd<D, CAUSAL, 8, 4>(p, q, k, v, o, lse, stream);
     if (long_kv && G % 2 == 0 && (long long)p.B * (p.Hq / 2) * ((p.Sq + 127) / 128) >= 512)
       return launch_fwd<D, CAUSAL, 8, 2>(p, q, k, v, o, lse, stream);
     if constexpr (!CAUSAL)

@@ -77,12 +77,14 @@ def test_parity_dit_self_workload(dev):
 
 # Shapes large enough to take the eight-wave forward workgroups: two query
 # heads of one KV head per workgroup (even group sizes, causal with the
-# diagonal off the tile grid, and non-causal), and 256 rows of one head
-# (non-causal, one query head per KV head).  Query and key lengths are
-# ragged; rows are sampled at the start, across workgroup boundaries (4096
-# is a multiple of both 128 and 256) and over the ragged end.
+# diagonal off the tile grid, and non-causal), four heads of 64 rows (causal,
+# group size 4, 520 workgroups), and 256 rows of one head (non-causal, one
+# query head per KV head).  Query and key lengths are ragged; rows are
+# sampled at the start, across workgroup boundaries in the middle (every
+# workgroup height divides 2048 and 4096) and over the ragged end.
 W8 = [
     wl("w8_head_pairs_causal", 1, 16, 4, 8100, 8292, 128, True, backward=False),
+    wl("w8_head_quads_causal", 1, 32, 8, 4100, 4200, 128, True, backward=False),
     wl("w8_head_pairs_noncausal_g2", 1, 16, 8, 8100, 2100, 128, False, backward=False),
     wl("w8_rows256_noncausal", 1, 16, 16, 8000, 2100, 128, False, backward=False),
 ]
@@ -90,7 +92,7 @@ W8 = [
 
 @pytest.mark.parametrize("w", W8, ids=[w.name for w in W8])
 def test_parity_eight_wave_forward(w, dev):
-    rows = list(range(0, 40)) + list(range(4000, 4200)) + list(range(w.Sq - 150, w.Sq))
+    rows = sorted(set(range(0, 40)) | set(range(w.Sq // 2 - 100, w.Sq // 2 + 100)) | set(range(w.Sq - 150, w.Sq)))
     H.check_sampled(w, dev, [(0, 0), (0, w.Hkv - 1)], rows_per_head=rows, backward=False)
 
 
