@@ -762,10 +762,15 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         if (j0 + kb0 >= Skv) break;  // no key of this half exists
         step(std::true_type{}, kb0);
       } else {
-        if (CAUSAL && (j0 + kb0 + 31 > qw0 + diag))
+        // Near the diagonal a half can lie wholly past this wave's last
+        // query (its dS is all zero): that wave skips it, which leaves its
+        // SIMD to the other workgroup's wave.
+        if (CAUSAL && (j0 + kb0 > qw0 + 31 + diag)) {
+        } else if (CAUSAL && (j0 + kb0 + 31 > qw0 + diag)) {
           step(std::true_type{}, kb0);
-        else
+        } else {
           step(std::false_type{}, kb0);
+        }
       }
       // One half at a time: interleaving the halves needs more registers
       // than two waves per SIMD have.
