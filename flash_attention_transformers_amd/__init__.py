@@ -103,27 +103,76 @@ def _stream_handle(t, stream) -> int:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _shapes(q, k):
-    if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q, k, v must be 4-D [B, H, S, D] tensors")
+def _shapes(q, k, v=None):
+    """Problem sizes from q [B,Hq,Sq,D] and k [B,Hkv,Skv,D]; v, when given,
+    must match k exactly."""
+    for n, t in (("q", q), ("k", k)) + ((("v", v),) if v is not None else ()):
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be a 4-D [B, H, S, D] tensor, got shape {tuple(t.shape)}")
     B, Hq, Sq, D = q.shape
-    _, Hkv, Skv, _ = k.shape
+    Bk, Hkv, Skv, Dk = k.shape
+    if Bk != B or Dk != D:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in batch or head dim")
+    if v is not None and tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"v must have k's shape {tuple(k.shape)}, got {tuple(v.shape)}")
     return B, Hq, Hkv, Sq, Skv, D
 
 
+def _expect(name, t, shape, dtype):
+    """`t` must have exactly `shape` and `dtype`."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
 def _require(*ts):
+    """Every tensor on one GPU and contiguous (BHSD row-major)."""
+    dev = None
     for t in ts:
         if not t.is_cuda:
             raise ValueError("libmattn tensors must live on the GPU")
         if not t.is_contiguous():
             raise ValueError("libmattn tensors must be contiguous (BHSD row-major)")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"libmattn tensors must share one device: {t.device} and {dev}")
+
+
+def _check_dense(q, k, v, o=None, lse=None, do=None, dq=None, dk=None, dv=None):
+    """Shapes and dtypes of a dense call, checked before any device check or
+    launch: the C side cannot see buffer extents, so a tensor smaller than
+    the sizes imply would be read or written out of bounds."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k, v)
+    for n, t in (("k", k), ("v", v)):
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} must have q's dtype {q.dtype}, got {t.dtype}")
+    for n, t in (("o", o), ("do", do), ("dq", dq)):
+        if t is not None:
+            _expect(n, t, q.shape, q.dtype)
+    for n, t in (("dk", dk), ("dv", dv)):
+        if t is not None:
+            _expect(n, t, k.shape, q.dtype)
+    if lse is not None:
+        _expect("lse", lse, (B, Hq, Sq), torch.float32)
+    return B, Hq, Hkv, Sq, Skv, D
+
+
+def _workspace_bytes(workspace, need: int) -> int:
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace holds {nbytes} bytes, the call needs {need}")
+    return nbytes
 
 
 def mattn_fwd(q, k, v, o, lse, causal: bool = False, scale: Optional[float] = None,
               stream=None) -> None:
     """Forward into pre-allocated o [B,Hq,Sq,D] and lse [B,Hq,Sq] (float32)."""
+    B, Hq, Hkv, Sq, Skv, D = _check_dense(q, k, v, o=o, lse=lse)
     _require(q, k, v, o, lse)
-    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     st = load_library().mattn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
@@ -136,11 +185,11 @@ def mattn_bwd(q, k, v, o, lse, do, dq, dk, dv, workspace, causal: bool = False,
               scale: Optional[float] = None, stream=None) -> None:
     """Backward into pre-allocated dq, dk, dv; `workspace` is a uint8 device
     tensor of at least mattn_bwd_workspace_size() bytes."""
+    B, Hq, Hkv, Sq, Skv, D = _check_dense(q, k, v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv)
+    nbytes = _workspace_bytes(workspace, mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D))
     _require(q, k, v, o, lse, do, dq, dk, dv, workspace)
-    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    nbytes = workspace.numel() * workspace.element_size()
     st = load_library().mattn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                   lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                                   dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D, int(causal),
@@ -155,11 +204,11 @@ def mattn_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, workspace, stages: int,
     order preprocess, dQ, dK/dV (separate calls follow the same order).  The
     bf16 dQ stage also forms the per-row D itself, so mattn_bwd enqueues dQ
     and dK/dV for bf16 and all three for fp32; the results are the same bits."""
+    B, Hq, Hkv, Sq, Skv, D = _check_dense(q, k, v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv)
+    nbytes = _workspace_bytes(workspace, mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D))
     _require(q, k, v, o, lse, do, dq, dk, dv, workspace)
-    B, Hq, Hkv, Sq, Skv, D = _shapes(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    nbytes = workspace.numel() * workspace.element_size()
     st = load_library().mattn_bwd_stages(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                          lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
                                          dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Sq, Skv, D,
@@ -185,17 +234,35 @@ def mattn_fwd_kvcache(q, k_cache, v_cache, block_table, seqlens_k, o, lse, works
     (or None when that is 0)."""
     import torch
 
-    _require(q, k_cache, v_cache, block_table, seqlens_k, o, lse)
+    for n, t in (("q", q), ("k_cache", k_cache)):
+        if t.dim() != 4:
+            raise ValueError(f"{n} must be a 4-D tensor, got shape {tuple(t.shape)}")
+    B, Hq, Sq, D = q.shape
+    num_pages, Hkv, page_size, Dc = k_cache.shape
+    if Dc != D:
+        raise ValueError(f"k_cache head dim {Dc} does not match q's {D}")
+    _expect("v_cache", v_cache, k_cache.shape, q.dtype)
+    _expect("k_cache", k_cache, k_cache.shape, q.dtype)
+    _expect("o", o, q.shape, q.dtype)
+    _expect("lse", lse, (B, Hq, Sq), torch.float32)
     if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
         raise TypeError("block_table and seqlens_k must be int32")
-    B, Hq, Sq, D = q.shape
-    num_pages, Hkv, page_size, _ = k_cache.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [B={B}, pages_per_seq], got {tuple(block_table.shape)}")
+    if seqlens_k.dim() != 1 or seqlens_k.shape[0] != B:
+        raise ValueError(f"seqlens_k must hold B={B} values, got shape {tuple(seqlens_k.shape)}")
     pages_per_seq = block_table.shape[1]
+    need = mattn_fwd_kvcache_workspace_size(B, Hq, Hkv, Sq, D, page_size, pages_per_seq)
+    if workspace is not None:
+        _workspace_bytes(workspace, need)
+    elif need > 0:
+        raise ValueError(f"this call needs a workspace of {need} bytes")
+    _require(q, k_cache, v_cache, block_table, seqlens_k, o, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     ws_ptr, ws_bytes = 0, 0
     if workspace is not None:
-        _require(workspace)
+        _require(q, workspace)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     st = load_library().mattn_fwd_kvcache(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                                           block_table.data_ptr(), seqlens_k.data_ptr(),

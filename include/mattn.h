@@ -87,9 +87,11 @@ size_t mattn_bwd_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D);
  * dk, dv [B,Hkv,Skv,D] in `dtype` (overwritten).  `workspace` is caller-owned
  * device memory of at least mattn_bwd_workspace_size() bytes; its contents on
  * entry do not matter.  Enqueues, on `stream` and with no host
- * synchronisation: the D = sum(dO * O) preprocess, the dK/dV kernel (plus a
- * fixed-order reduction of partials when the query range is split) and the dQ
- * kernel.  Results are bitwise reproducible run to run. */
+ * synchronisation, for bf16: the dQ kernel, which also forms the per-row
+ * statistic D = sum(dO * O) and stores it in the workspace, then the dK/dV
+ * kernel (plus a fixed-order reduction of partials when the query range is
+ * split), which reads D; for fp32: the D preprocess, then the dQ kernel,
+ * then the dK/dV kernel.  Results are bitwise reproducible run to run. */
 mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* o,
                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
                        int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,

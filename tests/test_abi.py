@@ -184,3 +184,124 @@ def test_kvcache_workspace_size():
         if o_b + l_b == n:
             ns = cand
     assert ns is not None and ns <= 25  # at least four 64-token tiles per split
+
+
+# The binding checks every tensor's shape and dtype against the sizes the C
+# call will be given, before its device check and before any launch (the C
+# side cannot see buffer extents).  CPU tensors reach those checks first, so
+# each mismatch below must raise its own error, not the device error.
+def _dense(B=1, Hq=4, Hkv=2, Sq=16, Skv=24, D=64, dtype=None):
+    import torch
+
+    dt = dtype or torch.bfloat16
+    q = torch.zeros(B, Hq, Sq, D, dtype=dt)
+    k = torch.zeros(B, Hkv, Skv, D, dtype=dt)
+    return dict(q=q, k=k, v=k.clone(), o=torch.zeros_like(q), lse=torch.zeros(B, Hq, Sq),
+                do=torch.zeros_like(q), dq=torch.zeros_like(q), dk=torch.zeros_like(k),
+                dv=torch.zeros_like(k), workspace=torch.zeros(1 << 16, dtype=torch.uint8))
+
+
+def _bad(name, fn):
+    import torch
+
+    t = _dense()
+    return t, name, fn(t, torch)
+
+
+DENSE_MISMATCH = {
+    "v_shorter_than_k": lambda t, torch: torch.zeros(1, 2, 23, 64, dtype=torch.bfloat16),
+    "v_other_dtype": lambda t, torch: torch.zeros(1, 2, 24, 64, dtype=torch.float32),
+    "k_other_head_dim": lambda t, torch: torch.zeros(1, 2, 24, 128, dtype=torch.bfloat16),
+    "k_other_batch": lambda t, torch: torch.zeros(2, 2, 24, 64, dtype=torch.bfloat16),
+    "o_short": lambda t, torch: torch.zeros(1, 4, 15, 64, dtype=torch.bfloat16),
+    "o_other_dtype": lambda t, torch: torch.zeros(1, 4, 16, 64, dtype=torch.float32),
+    "lse_bf16": lambda t, torch: torch.zeros(1, 4, 16, dtype=torch.bfloat16),
+    "lse_short": lambda t, torch: torch.zeros(1, 4, 15),
+    "lse_4d": lambda t, torch: torch.zeros(1, 4, 16, 1),
+    "q_3d": lambda t, torch: torch.zeros(4, 16, 64, dtype=torch.bfloat16),
+}
+FWD_TARGET = {"v_shorter_than_k": "v", "v_other_dtype": "v", "k_other_head_dim": "k",
+              "k_other_batch": "k", "o_short": "o", "o_other_dtype": "o", "lse_bf16": "lse",
+              "lse_short": "lse", "lse_4d": "lse", "q_3d": "q"}
+
+
+@pytest.mark.parametrize("case", sorted(DENSE_MISMATCH))
+def test_binding_fwd_rejects_mismatched_tensors(case):
+    t, _, bad = _bad(case, DENSE_MISMATCH[case])
+    t[FWD_TARGET[case]] = bad
+    with pytest.raises(ValueError) as e:
+        fa.mattn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"])
+    assert "GPU" not in str(e.value), e.value
+
+
+BWD_MISMATCH = {
+    "do": lambda torch: torch.zeros(1, 4, 16, 32, dtype=torch.bfloat16),
+    "dq": lambda torch: torch.zeros(1, 4, 17, 64, dtype=torch.bfloat16),
+    "dk": lambda torch: torch.zeros(1, 4, 24, 64, dtype=torch.bfloat16),
+    "dv": lambda torch: torch.zeros(1, 2, 24, 64, dtype=torch.float32),
+    "lse": lambda torch: torch.zeros(1, 4, 16, dtype=torch.float64),
+    "workspace": lambda torch: torch.zeros(16, dtype=torch.uint8),
+}
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MISMATCH))
+@pytest.mark.parametrize("call", ["bwd", "bwd_stages"])
+def test_binding_bwd_rejects_mismatched_tensors(name, call):
+    import torch
+
+    t = _dense()
+    t[name] = BWD_MISMATCH[name](torch)
+    args = [t[n] for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv", "workspace")]
+    with pytest.raises(ValueError) as e:
+        if call == "bwd":
+            fa.mattn_bwd(*args)
+        else:
+            fa.mattn_bwd_stages(*args, fa.MATTN_BWD_ALL)
+    assert "GPU" not in str(e.value), e.value
+
+
+def _paged(B=2, Hq=8, Hkv=2, Sq=1, D=128, num_pages=6, page_size=64, pps=3):
+    import torch
+
+    q = torch.zeros(B, Hq, Sq, D, dtype=torch.bfloat16)
+    kc = torch.zeros(num_pages, Hkv, page_size, D, dtype=torch.bfloat16)
+    return dict(q=q, k_cache=kc, v_cache=kc.clone(),
+                block_table=torch.zeros(B, pps, dtype=torch.int32),
+                seqlens_k=torch.zeros(B, dtype=torch.int32), o=torch.zeros_like(q),
+                lse=torch.zeros(B, Hq, Sq), workspace=torch.zeros(1 << 20, dtype=torch.uint8))
+
+
+PAGED_MISMATCH = {
+    "block_table": lambda torch: torch.zeros(3, 3, dtype=torch.int32),
+    "seqlens_k": lambda torch: torch.zeros(1, dtype=torch.int32),
+    "v_cache": lambda torch: torch.zeros(5, 2, 64, 128, dtype=torch.bfloat16),
+    "k_cache": lambda torch: torch.zeros(6, 2, 64, 64, dtype=torch.bfloat16),
+    "o": lambda torch: torch.zeros(2, 8, 2, 128, dtype=torch.bfloat16),
+    "lse": lambda torch: torch.zeros(2, 8, 1, dtype=torch.bfloat16),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PAGED_MISMATCH))
+def test_binding_kvcache_rejects_mismatched_tensors(name):
+    import torch
+
+    t = _paged()
+    t[name] = PAGED_MISMATCH[name](torch)
+    with pytest.raises(ValueError) as e:
+        fa.mattn_fwd_kvcache(t["q"], t["k_cache"], t["v_cache"], t["block_table"], t["seqlens_k"],
+                             t["o"], t["lse"], t["workspace"])
+    assert "GPU" not in str(e.value), e.value
+
+
+def test_binding_accepts_matching_tensors_up_to_the_device_check():
+    # Consistent CPU tensors pass every shape check and stop at the device check.
+    t = _dense()
+    with pytest.raises(ValueError, match="GPU"):
+        fa.mattn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"])
+    with pytest.raises(ValueError, match="GPU"):
+        fa.mattn_bwd(*[t[n] for n in ("q", "k", "v", "o", "lse", "do", "dq", "dk", "dv",
+                                       "workspace")])
+    p = _paged()
+    with pytest.raises(ValueError, match="GPU"):
+        fa.mattn_fwd_kvcache(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seqlens_k"],
+                             p["o"], p["lse"], p["workspace"])
