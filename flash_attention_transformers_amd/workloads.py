@@ -83,9 +83,12 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     generator and are not handled specially.
     """
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = (bits + 0x7FFF + lsb) >> 16
+    bits = x.view(np.uint32)
+    # For finite x the sum stays below 2^32 (the largest finite pattern,
+    # 0xFF7FFFFF, plus 0x8000), so 32-bit arithmetic is exact.
+    rounded = bits + np.uint32(0x7FFF)
+    rounded += (bits >> np.uint32(16)) & np.uint32(1)
+    rounded >>= np.uint32(16)
     return rounded.astype(np.uint16)
 
 

@@ -223,3 +223,54 @@ def test_stage_sequence_equals_bwd(shape, dev):
     torch.cuda.synchronize()
     for n, x in (("dq", dq), ("dk", dk), ("dv", dv)):
         assert torch.equal(x.view(torch.int16), ref[n].view(torch.int16)), n
+
+
+@pytest.mark.parametrize("shape", [(2, 4, 2, 200, 260, 128, True, "bf16"),
+                                   (1, 8, 2, 300, 257, 128, False, "bf16"),
+                                   (1, 2, 2, 150, 90, 64, False, "f32"),
+                                   (1, 4, 2, 130, 130, 128, True, "f32")])
+def test_key_translation_invariance(shape, dev):
+    """Adding one vector c to every key of a KV head leaves O, dQ, dK and dV
+    unchanged (the softmax is shift-invariant per query row) and moves LSE_i
+    by scale * <q_i, c>.  Keys and c are multiples of 1/8 with small
+    magnitude, so k + c is exact in bf16 and both runs see exactly the
+    translated problem.  Each output is compared between the two runs within
+    its parity tolerance relative to the tensor's norm; LSE within twice its
+    tolerance (each run carries its own error)."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D, causal, dtype = shape
+    H.say(f"[key translation] {shape}")
+    rng = np.random.default_rng(29)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+
+    def dev_t(a):
+        return torch.from_numpy(np.asarray(a, np.float32)).to(dev).to(tdt).contiguous()
+
+    q = dev_t(rng.standard_normal((B, Hq, Sq, D), dtype=np.float32))
+    v = dev_t(rng.standard_normal((B, Hkv, Skv, D), dtype=np.float32))
+    do = dev_t(rng.standard_normal((B, Hq, Sq, D), dtype=np.float32))
+    k_np = rng.integers(-16, 17, size=(B, Hkv, Skv, D)).astype(np.float32) / 8
+    c_np = rng.integers(-8, 9, size=(B, Hkv, 1, D)).astype(np.float32) / 8
+    k, k2 = dev_t(k_np), dev_t(k_np + c_np)
+    scale = D ** -0.5
+    a = fwd_bwd(dict(q=q, k=k, v=v, do=do), causal, scale)
+    b = fwd_bwd(dict(q=q, k=k2, v=v, do=do), causal, scale)
+    torch.cuda.synchronize()
+    tol = H.TOL[dtype]
+    qh = q.float().cpu().numpy().astype(np.float64)
+    shift = scale * np.einsum("bhsd,bhd->bhs", qh,
+                              np.repeat(c_np[:, :, 0, :].astype(np.float64), Hq // Hkv, axis=1))
+    lse_err = np.abs(H.to_np(b["lse"]) - H.to_np(a["lse"]) - shift).max()
+    res = {"o_max_abs": H.max_abs(H.to_np(b["o"]), H.to_np(a["o"])),
+           "o_rel_l2": H.rel_l2(H.to_np(b["o"]), H.to_np(a["o"])),
+           "lse_shift_max_abs": float(lse_err)}
+    for n in ("dq", "dk", "dv"):
+        res[n] = H.rel_l2(H.to_np(b[n]), H.to_np(a[n]))
+    H.say(f"    {res}")
+    H.RESULTS.append((f"key_translation_{'x'.join(map(str, shape))}", "invariance", res))
+    assert res["o_max_abs"] <= tol["o_max_abs"], res
+    assert res["o_rel_l2"] <= tol["o_rel_l2"], res
+    assert res["lse_shift_max_abs"] <= 2 * tol["lse_max_abs"], res
+    for n in ("dq", "dk", "dv"):
+        assert res[n] <= tol["grad_rel_l2"], (n, res)
