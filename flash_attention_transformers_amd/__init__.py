@@ -23,6 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmattn.so")
 
 MATTN_OK, MATTN_ERR_INVALID_ARG, MATTN_ERR_UNSUPPORTED, MATTN_ERR_LAUNCH = 0, 1, 2, 3
+MATTN_ERR_SCRATCH = 4
+MATTN_SCRATCH_BYTES = 128 << 20  # static backward scratch of mattn_bwd_noalloc
 MATTN_BF16, MATTN_F32 = 0, 1
 MATTN_BWD_PREPROCESS, MATTN_BWD_DKDV, MATTN_BWD_DQ = 1, 2, 4
 MATTN_BWD_ALL = MATTN_BWD_PREPROCESS | MATTN_BWD_DKDV | MATTN_BWD_DQ
@@ -53,6 +55,9 @@ def load_library() -> ctypes.CDLL:
     lib.mattn_bwd_stages.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
                                      i, vp, sz, ctypes.c_uint, vp]
     lib.mattn_bwd_stages.restype = i
+    lib.mattn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f,
+                                      i, vp]
+    lib.mattn_bwd_noalloc.restype = i
     lib.mattn_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.mattn_bwd_workspace_size.restype = sz
     lib.mattn_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, i,

@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "mattn.h"
 #include "kernels.hpp"
@@ -55,6 +56,46 @@ size_t part_bytes(int B, int Hkv, int Sq, int Skv, int D) {
   if (ns <= 1) return 0;
   const size_t n_kt = (size_t)(Skv + mattn::BWD_BN - 1) / mattn::BWD_BN;
   return round256(2 * (size_t)ns * B * Hkv * n_kt * mattn::BWD_BN * D * sizeof(float));
+}
+
+// Backward workspace for mattn_bwd_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, not a device address; its address on a device comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = (size_t)MATTN_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The device the stream's work runs on (the current device for the null stream).
+hipError_t stream_device(hipStream_t stream, int* dev) {
+  return stream ? hipStreamGetDevice(stream, dev) : hipGetDevice(dev);
+}
+
+// Device address of `scratch` on device `dev`.
+hipError_t scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -147,6 +188,29 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
                           scale, dtype, workspace, workspace_bytes, stages, stream);
 }
 
+mattn_status mattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                               float scale, mattn_dtype dtype, hipStream_t stream) {
+  Sizes sz;
+  mattn_status st = check_args(B, Hq, Hkv, Sq, Skv, D, causal, scale, dtype, &sz);
+  if (st != MATTN_OK) return st;
+  if (sz.kv_elems > 0 && !ptrs_ok({dk, dv})) return MATTN_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (sz.rows > 0) {
+    if (!ptrs_ok({q, k, v, o, lse, dout, dq})) return MATTN_ERR_INVALID_ARG;
+    if (mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D) > kScratchBytes) return MATTN_ERR_SCRATCH;
+    int dev = 0;
+    if (stream_device(stream, &dev) != hipSuccess || scratch_on(dev, &ws) != hipSuccess)
+      return MATTN_ERR_LAUNCH;
+  }
+  // The workspace contents on entry do not matter to the backward (every
+  // value it reads there was written earlier in the same call), so the
+  // scratch needs no clearing between calls.
+  return mattn_bwd(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Sq, Skv, D, causal, scale,
+                   dtype, ws, kScratchBytes, stream);
+}
+
 size_t mattn_fwd_kvcache_workspace_size(int B, int Hq, int Hkv, int Sq, int D, int page_size,
                                         int pages_per_seq) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || Sq <= 0 || page_size <= 0 || pages_per_seq <= 0 ||
@@ -197,6 +261,9 @@ const char* mattn_strerror(mattn_status s) {
     case MATTN_ERR_INVALID_ARG: return "invalid argument";
     case MATTN_ERR_UNSUPPORTED: return "unsupported problem (head dim, size or causal Sq > Skv)";
     case MATTN_ERR_LAUNCH: return "HIP kernel launch failed";
+    case MATTN_ERR_SCRATCH:
+      return "problem needs more backward workspace than the static scratch buffer holds "
+             "(MATTN_SCRATCH_BYTES); call mattn_bwd with a workspace";
   }
   return "unknown status";
 }

@@ -27,8 +27,10 @@
  * throughout; no operand is rounded below float32).
  *
  * Ownership: every pointer is a device pointer owned by the caller.  The
- * library allocates nothing, keeps no global state, never synchronises the
- * device and is safe to call from several host threads.  Work is enqueued on
+ * library allocates nothing, never synchronises the device and is safe to
+ * call from several host threads.  Its only global state is the static
+ * scratch array of mattn_bwd_noalloc (below) and that array's per-device
+ * address, looked up once.  Work is enqueued on
  * `stream` (0 = the null stream) and runs asynchronously; buffers must stay
  * alive until the stream reaches that point.  Outputs must not alias inputs
  * and are fully overwritten (never accumulated into).
@@ -46,6 +48,8 @@
  *                          elements, or causal with Sq > Skv (which would
  *                          leave query rows with no visible key).
  *   MATTN_ERR_LAUNCH       the HIP runtime reported an error after a launch.
+ *   MATTN_ERR_SCRATCH      (mattn_bwd_noalloc only) the problem needs more
+ *                          workspace than the library's static scratch holds.
  * B*Hq*Sq == 0 with otherwise valid sizes returns MATTN_OK: the forward does
  * nothing and the backward writes zeros to dk and dv.
  */
@@ -63,7 +67,8 @@ typedef enum {
   MATTN_OK = 0,
   MATTN_ERR_INVALID_ARG = 1,
   MATTN_ERR_UNSUPPORTED = 2,
-  MATTN_ERR_LAUNCH = 3
+  MATTN_ERR_LAUNCH = 3,
+  MATTN_ERR_SCRATCH = 4
 } mattn_status;
 
 typedef enum { MATTN_BF16 = 0, MATTN_F32 = 1 } mattn_dtype;
@@ -97,6 +102,26 @@ mattn_status mattn_bwd(const void* q, const void* k, const void* v, const void* 
                        int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
                        float scale, mattn_dtype dtype, void* workspace,
                        size_t workspace_bytes, hipStream_t stream);
+
+/* mattn_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, allocation-free serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments (minus the
+ * workspace), checks, kernels and results as mattn_bwd (the same bits).  The
+ * workspace is a static device array of MATTN_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; its device address is
+ * looked up once per device on the first call there.  The call allocates
+ * nothing (no hipMalloc, hipFree or allocating library routine).
+ * A problem whose mattn_bwd_workspace_size() exceeds MATTN_SCRATCH_BYTES
+ * returns MATTN_ERR_SCRATCH before anything is enqueued.  Every call on one
+ * GPU shares that GPU's array: calls whose work may overlap on one GPU
+ * (different streams, or different host threads without ordering) race and
+ * give wrong results; calls on one stream are ordered and safe.  The stream
+ * must belong to the device whose array is used (the stream's device). */
+#define MATTN_SCRATCH_BYTES (128u << 20)
+mattn_status mattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                               int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                               float scale, mattn_dtype dtype, hipStream_t stream);
 
 /* The stages mattn_bwd enqueues, selectable for callers that schedule or
  * time them separately.  Same arguments, checks and workspace as mattn_bwd;

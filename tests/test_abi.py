@@ -27,7 +27,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["mattn_fwd", "mattn_bwd", "mattn_bwd_stages", "mattn_bwd_workspace_size", "mattn_strerror",
-         "mattn_version", "mattn_fwd_kvcache", "mattn_fwd_kvcache_workspace_size"])
+         "mattn_version", "mattn_fwd_kvcache", "mattn_fwd_kvcache_workspace_size",
+         "mattn_bwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -39,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 def test_version_and_strerror():
     assert fa.mattn_version() >= 100
     assert fa.mattn_strerror(0) == "success"
-    for s in (1, 2, 3):
+    for s in (1, 2, 3, 4):
         assert fa.mattn_strerror(s) and fa.mattn_strerror(s) != "success"
     assert fa.mattn_strerror(99) == "unknown status"
 
@@ -305,3 +306,38 @@ def test_binding_accepts_matching_tensors_up_to_the_device_check():
     with pytest.raises(ValueError, match="GPU"):
         fa.mattn_fwd_kvcache(p["q"], p["k_cache"], p["v_cache"], p["block_table"], p["seqlens_k"],
                              p["o"], p["lse"], p["workspace"])
+
+
+def noalloc_status(B=1, Hq=2, Hkv=2, Sq=128, Skv=128, D=64, causal=0, scale=0.125, dtype=0, q=P,
+                   dq=P, dk=P):
+    lib = fa.load_library()
+    return lib.mattn_bwd_noalloc(q, P, P, P, P, P, dq, dk, P, B, Hq, Hkv, Sq, Skv, D, causal, scale,
+                                 dtype, None)
+
+
+@pytest.mark.parametrize("kw", [dict(B=-1), dict(Hq=3, Hkv=2), dict(causal=2), dict(q=0),
+                                dict(dq=P + 4), dict(dk=0), dict(scale=float("nan"))])
+def test_noalloc_rejects_invalid(kw):
+    # rejected before the scratch lookup and before any launch
+    assert noalloc_status(**kw) == fa.MATTN_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_unsupported():
+    assert noalloc_status(D=96) == fa.MATTN_ERR_UNSUPPORTED
+    assert noalloc_status(causal=1, Sq=300, Skv=200) == fa.MATTN_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_problems_beyond_the_scratch():
+    # Dlt of 3 * 5592405 rows (64 MiB) plus split partials exceeds the 128 MiB array.
+    B, Hq, Hkv, Sq, Skv, D = 1, 3, 3, 5592405, 100, 128
+    assert fa.mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D) > fa.MATTN_SCRATCH_BYTES
+    assert noalloc_status(B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Skv=Skv, D=D) == fa.MATTN_ERR_SCRATCH
+    # the largest backward workspace among the workloads (DiT cross, 257 keys) fits
+    assert fa.mattn_bwd_workspace_size(1, 10, 10, 32760, 257, 128) < fa.MATTN_SCRATCH_BYTES
+    assert "scratch" in fa.mattn_strerror(fa.MATTN_ERR_SCRATCH)
+
+
+def test_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MATTN_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.MATTN_SCRATCH_BYTES
