@@ -4,10 +4,19 @@ One step = mattn_fwd + the backward (the dQ kernel, which also forms
 D = sum(dO*O) for bf16, then the dK/dV kernel) over one batch of seeded
 synthetic input that is already resident in HBM.  The backward is enqueued as
 its stages (mattn_bwd_stages, the same kernels mattn_bwd issues, in the same
-order on the same stream).  The
-timed region holds exactly `steps` steps and nothing else; a second pass of
-the same steps with HIP events between the kernels gives the per-kernel
-times, and a pass of forwards alone gives the forward's share.
+order on the same stream).  The timed region holds exactly `steps` steps and
+nothing else, run as 3 consecutive groups with HIP events between them; the
+figure is the median of the group means (the LingBot report's timing
+protocol: groups of event timings, median of the group means).  The forward
+alone is timed the same way to split the step into forward and backward, and
+a second pass with events between the kernels gives the per-kernel times.
+Clocks (sclk, mclk) are read before and after.
+
+With the default workload the same run also measures, each with its own
+warm-up and 3 groups: the DiT self-attention forward, the two DiT
+cross-attention shapes and the decoder shape, the latter three warm and with
+inputs rotated through more than 1 GiB (beyond the 256 MB last-level cache),
+each against its roofline; they appear under "workloads" in the same line.
 
 Default workload: GQA causal training attention, B=4, Hq=32, Hkv=8, S=4096,
 D=128, bf16 (the long-sequence configuration that exercises every step of the
@@ -16,7 +25,7 @@ path, including the grouped-KV head map and the group-summed backward).
 Prints ONE JSON line.  `value` is credited TFLOP/s of the whole step:
 (4*B*Hq*Sq*Skv*D forward + 2.5x that backward, halved for causal) / step time.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu] [--no-extra]
     python bench.py --copy-probe   # plain 1 GiB device copy, to calibrate HBM byte counters
     python bench.py --gemm-probe   # library bf16 GEMM rate: what a plain contraction reaches here
 
@@ -300,6 +309,248 @@ def main_paged(args, w):
     print(json.dumps(line), flush=True)
 
 
+def read_clocks():
+    """Current GPU clocks: sclk from torch (amdsmi), sclk and mclk as rocm-smi
+    reports them.  Either may be None where the tool is unavailable."""
+    import subprocess
+
+    import torch
+
+    out = {"sclk_mhz": None, "rocm_smi": None}
+    try:
+        out["sclk_mhz"] = int(torch.cuda.clock_rate(0))
+    except Exception:  # pragma: no cover - tool missing
+        pass
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout)
+        card = {}
+        for _, vals in sorted(data.items()):
+            for key, val in vals.items():
+                k = key.lower()
+                if k.startswith(("sclk", "mclk", "fclk")):
+                    card[key.strip(" :")] = val
+            break
+        out["rocm_smi"] = card or None
+    except Exception:  # pragma: no cover
+        pass
+    return out
+
+
+def time_groups(fn, steps: int, stream, groups: int = 3, during=None):
+    """Run fn(i) for i in [0, steps) as `groups` consecutive groups inside
+    one synchronized region, with HIP events recorded on `stream` between
+    the groups.  Returns (mean ms per call of each group, wall seconds).
+    `during`, if given, is called once every call is enqueued and before the
+    synchronize, while the GPU still works through them."""
+    import torch
+
+    groups = max(1, min(groups, steps))
+    bounds = [steps * g // groups for g in range(groups + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    evs[0].record(stream)
+    for g in range(groups):
+        for i in range(bounds[g], bounds[g + 1]):
+            fn(i)
+        evs[g + 1].record(stream)
+    if during is not None:
+        during()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    means = [evs[g].elapsed_time(evs[g + 1]) / (bounds[g + 1] - bounds[g]) for g in range(groups)]
+    return means, wall
+
+
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def algo_bytes(w):
+    """Algorithmic HBM bytes (each tensor read or written once): forward reads
+    q, k, v and writes o and lse; the backward reads q, k, v, o, dO and lse
+    and writes dq, dk and dv (the per-row D workspace excluded)."""
+    e = 2 if w.dtype == "bf16" else 4
+    q = w.B * w.Hq * w.Sq * w.D * e
+    kv = w.B * w.Hkv * w.Skv * w.D * e
+    lse = w.B * w.Hq * w.Sq * 4
+    return 2 * q + 2 * kv + lse, 4 * q + 4 * kv + lse
+
+
+class DenseRun:
+    """Device buffers of one workload (R copies when rotating inputs through
+    more memory than the last-level cache holds) and the calls of one step."""
+
+    def __init__(self, w, dev, stream, copies: int = 1):
+        import torch
+
+        import flash_attention_transformers_amd as fa
+        from flash_attention_transformers_amd import workloads as W
+
+        self.fa, self.w, self.stream = fa, w, stream
+        inp = W.make_inputs(w)
+        base = W.to_torch(inp, dev)
+        del inp
+        self.sets = []
+        for r in range(copies):
+            t = {n: (x if r == 0 else x.clone()) for n, x in base.items()}
+            t["o"] = torch.empty_like(t["q"])
+            t["lse"] = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=dev)
+            if w.backward:
+                t["dq"], t["dk"], t["dv"] = (torch.empty_like(t["q"]), torch.empty_like(t["k"]),
+                                             torch.empty_like(t["v"]))
+                t["ws"] = fa.bwd_workspace(t["q"], t["k"])
+            self.sets.append(t)
+        # The stages mattn_bwd enqueues: bf16 forms D inside the dQ kernel.
+        if not w.backward:
+            self.stages, self.names = [], ["fwd"]
+        elif w.dtype == "bf16":
+            self.stages, self.names = [fa.MATTN_BWD_DQ, fa.MATTN_BWD_DKDV], ["fwd", "dq", "dkdv"]
+        else:
+            self.stages = [fa.MATTN_BWD_PREPROCESS, fa.MATTN_BWD_DQ, fa.MATTN_BWD_DKDV]
+            self.names = ["fwd", "pre", "dq", "dkdv"]
+
+    def footprint(self) -> int:
+        return sum(x.numel() * x.element_size() for x in self.sets[0].values())
+
+    def fwd(self, i: int):
+        t, w = self.sets[i % len(self.sets)], self.w
+        self.fa.mattn_fwd(t["q"], t["k"], t["v"], t["o"], t["lse"], w.causal, w.scale, self.stream)
+
+    def step(self, i: int, ev=None):
+        t, w = self.sets[i % len(self.sets)], self.w
+        if ev is not None:
+            ev[0].record(self.stream)
+        self.fwd(i)
+        if ev is not None:
+            ev[1].record(self.stream)
+        for j, st in enumerate(self.stages):
+            self.fa.mattn_bwd_stages(t["q"], t["k"], t["v"], t["o"], t["lse"], t["do"], t["dq"],
+                                     t["dk"], t["dv"], t["ws"], st, w.causal, w.scale, self.stream)
+            if ev is not None:
+                ev[2 + j].record(self.stream)
+
+    def kernel_ms(self, steps: int):
+        """Per-kernel spans: `steps` steps with an event between kernels."""
+        import torch
+
+        nev = 2 + len(self.stages)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(steps)]
+        for i in range(steps):
+            self.step(i, evs[i])
+        torch.cuda.synchronize()
+        return {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps
+                for i, n in enumerate(self.names)}
+
+
+def sclk_now():
+    """The GPU's current shader clock in MHz (amdsmi through torch), or None."""
+    import torch
+
+    try:
+        return int(torch.cuda.clock_rate(0))
+    except Exception:  # pragma: no cover
+        return None
+
+
+def measure(run: DenseRun, steps: int, warmup: int, clocks=None):
+    """Warm up, then the step and the forward alone, each as 3 groups; the
+    median of the group means is the figure.  With `clocks` (a list), the
+    shader clock sampled while the timed steps run is appended to it."""
+    import torch
+
+    for i in range(max(warmup, len(run.sets))):
+        run.step(i)
+    torch.cuda.synchronize()
+    during = None if clocks is None else (lambda: clocks.append(sclk_now()))
+    step_groups, wall = time_groups(run.step, steps, run.stream, during=during)
+    fwd_groups, _ = time_groups(run.fwd, steps, run.stream)
+    return step_groups, fwd_groups, wall
+
+
+def summarize(w, step_groups, fwd_groups, peak):
+    ms_step = median(step_groups)
+    fwd_ms = median(fwd_groups)
+    fwd_flop = w.fwd_flop()
+    out = {
+        "ms_per_step": round(ms_step, 4),
+        "step_group_ms": [round(x, 4) for x in step_groups],
+        "fwd_ms": round(fwd_ms, 4),
+        "fwd_group_ms": [round(x, 4) for x in fwd_groups],
+        "fwd_tflops": round(fwd_flop / (fwd_ms * 1e-3) / 1e12, 2),
+    }
+    out["fwd_pct_of_peak"] = round(100 * out["fwd_tflops"] / peak, 2)
+    if w.backward:
+        bwd_ms = ms_step - fwd_ms
+        out["bwd_ms"] = round(bwd_ms, 4)
+        out["bwd_tflops"] = round(w.bwd_flop() / (bwd_ms * 1e-3) / 1e12, 2)
+        out["bwd_pct_of_peak"] = round(100 * out["bwd_tflops"] / peak, 2)
+        out["step_tflops"] = round((fwd_flop + w.bwd_flop()) / (ms_step * 1e-3) / 1e12, 2)
+    return out
+
+
+def roofline_fracs(w, res, peak):
+    """Fraction of each direction's roofline: the larger of the time at the
+    MFMA peak for its credited FLOP and the time at the HBM peak for its
+    algorithmic bytes, over the measured time."""
+    fb, bb = algo_bytes(w)
+    out = {}
+    t_f = max(w.fwd_flop() / (peak * 1e12), fb / (HBM_PEAK_GBS * 1e9))
+    out["fwd_roofline_frac"] = round(t_f / (res["fwd_ms"] * 1e-3), 4)
+    out["fwd_bound"] = "hbm" if fb / (HBM_PEAK_GBS * 1e9) > w.fwd_flop() / (peak * 1e12) else "mfma"
+    if w.backward:
+        t_b = max(w.bwd_flop() / (peak * 1e12), bb / (HBM_PEAK_GBS * 1e9))
+        out["bwd_roofline_frac"] = round(t_b / (res["bwd_ms"] * 1e-3), 4)
+        out["bwd_bound"] = "hbm" if bb / (HBM_PEAK_GBS * 1e9) > w.bwd_flop() / (peak * 1e12) else "mfma"
+    out["fwd_algo_bytes"], out["bwd_algo_bytes"] = fb, (bb if w.backward else None)
+    return out
+
+
+# Workloads measured beside the default one in the same run: the DiT
+# self-attention forward (its own >= 50% gate), the two DiT cross-attention
+# shapes and the decoder shape against their rooflines, warm and with inputs
+# rotated through more memory than the 256 MB last-level cache.
+EXTRA = [("dit_self", False), ("dit_cross_512", True), ("dit_cross_257", True),
+         ("decoder_mha_causal", True)]
+ROTATE_BYTES = 1 << 30
+
+
+def extra_workloads(dev, stream, steps: int, warmup: int):
+    import torch
+
+    from flash_attention_transformers_amd import workloads as W
+
+    out = {}
+    for name, rotate in EXTRA:
+        w = W.WORKLOADS[name]
+        peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
+        run = DenseRun(w, dev, stream)
+        sg, fg, _ = measure(run, steps, warmup)
+        res = {"warm": summarize(w, sg, fg, peak)}
+        res["warm"].update(roofline_fracs(w, res["warm"], peak))
+        if rotate:
+            copies = -(-ROTATE_BYTES // run.footprint())
+            del run
+            torch.cuda.empty_cache()
+            run = DenseRun(w, dev, stream, copies=copies)
+            sg, fg, _ = measure(run, steps, warmup)
+            res["rotated"] = summarize(w, sg, fg, peak)
+            res["rotated"].update(roofline_fracs(w, res["rotated"], peak))
+            res["rotated"]["input_sets"] = copies
+            res["rotated"]["rotated_bytes"] = copies * run.footprint()
+        res["config"] = (f"B={w.B} Hq={w.Hq} Hkv={w.Hkv} Sq={w.Sq} Skv={w.Skv} D={w.D} "
+                         f"causal={int(w.causal)} {w.dtype} "
+                         + ("forward + backward" if w.backward else "forward only"))
+        out[name] = res
+        del run
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -307,6 +558,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_causal")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads measured beside the default one")
     ap.add_argument("--copy-probe", action="store_true", help="run the HBM calibration copy")
     ap.add_argument("--gemm-probe", action="store_true", help="time the library bf16 GEMM")
     args = ap.parse_args()
@@ -332,86 +585,32 @@ def main():
     w = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     fa.load_library()
-    inp = W.make_inputs(w)
-    t = W.to_torch(inp, dev)
-    del inp
-    q, k, v, do = t["q"], t["k"], t["v"], t["do"]
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = fa.bwd_workspace(q, k)
     stream = torch.cuda.current_stream(dev)
+    clocks_before = read_clocks()
+    run = DenseRun(w, dev, stream)
+    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
 
-    # The stages mattn_bwd enqueues: bf16 forms D inside the dQ kernel.
-    if not w.backward:
-        stages, names = [], ["fwd"]
-    elif w.dtype == "bf16":
-        stages, names = [fa.MATTN_BWD_DQ, fa.MATTN_BWD_DKDV], ["fwd", "dq", "dkdv"]
-    else:
-        stages = [fa.MATTN_BWD_PREPROCESS, fa.MATTN_BWD_DQ, fa.MATTN_BWD_DKDV]
-        names = ["fwd", "pre", "dq", "dkdv"]
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        fa.mattn_fwd(q, k, v, o, lse, w.causal, w.scale, stream)
-        if ev is not None:
-            ev[1].record(stream)
-        for i, st in enumerate(stages):
-            fa.mattn_bwd_stages(q, k, v, o, lse, do, dq, dk, dv, ws, st, w.causal, w.scale, stream)
-            if ev is not None:
-                ev[2 + i].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # Timed region: exactly `steps` steps, nothing else on the stream.
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
+    # Timed region: exactly `steps` steps in 3 consecutive groups, nothing
+    # else on the stream; the figure is the median of the group means.
+    during = []
+    step_groups, fwd_groups, wall = measure(run, args.steps, args.warmup, clocks=during)
+    res = summarize(w, step_groups, fwd_groups, peak)
+    ms_step = res["ms_per_step"]
     # Per-kernel breakdown: the same number of steps again, with an event
     # between consecutive kernels.  Each event costs ~12 us of stream time at
     # a kernel boundary, so these steps run a little longer than the timed
     # ones; kernel_ms[k] is the span between the events around kernel k.
-    nev = 2 + len(stages)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    kern_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-               for i, n in enumerate(names)}
-    # The forward alone, back to back (events only around the loop); the
-    # backward's share of the step is the rest.
-    f0 = torch.cuda.Event(enable_timing=True)
-    f1 = torch.cuda.Event(enable_timing=True)
-    f0.record(stream)
-    for _ in range(args.steps):
-        fa.mattn_fwd(q, k, v, o, lse, w.causal, w.scale, stream)
-    f1.record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = f0.elapsed_time(f1) / args.steps
-    bwd_ms = ms_step - fwd_ms if w.backward else None
+    kern_ms = run.kernel_ms(args.steps)
+    clocks_after = read_clocks()
 
     fwd_flop = w.fwd_flop()
     step_flop = fwd_flop + (w.bwd_flop() if w.backward else 0.0)
-    peak = BF16_PEAK_TFLOPS if w.dtype == "bf16" else F32_PEAK_TFLOPS
     value = step_flop / (ms_step * 1e-3) / 1e12
-    fwd_tf = fwd_flop / (fwd_ms * 1e-3) / 1e12
-    bwd_tf = w.bwd_flop() / (bwd_ms * 1e-3) / 1e12 if w.backward else None
 
     # Roofline of the kernel with the largest share of the step.
     F = fwd_flop
     per_launch = {"fwd": F, "dkdv": 2.0 * F, "dq": 1.5 * F}
-    dom = max((n for n in names if n in per_launch), key=lambda n: kern_ms[n])
+    dom = max((n for n in run.names if n in per_launch), key=lambda n: kern_ms[n])
     kname = roofline_kernel(dom, w.dtype)
     achieved = per_launch[dom] / (kern_ms[dom] * 1e-3) / 1e12
     roofline = {
@@ -431,7 +630,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -443,19 +642,34 @@ def main():
                         + ("forward + backward" if w.backward else "forward only"),
             "global_batch": w.B, "seq_len": w.Sq, "parallelism": "single GPU",
         },
+        "timing": "the timed steps run as 3 consecutive groups with HIP events between them; "
+                  "ms_per_step and fwd_ms are the medians of the group means (the forward "
+                  "alone is timed the same way after the steps)",
         "pct_of_peak": round(100 * value / peak, 2),
-        "fwd_tflops": round(fwd_tf, 2),
-        "fwd_pct_of_peak": round(100 * fwd_tf / peak, 2),
-        "bwd_tflops": None if bwd_tf is None else round(bwd_tf, 2),
-        "bwd_pct_of_peak": None if bwd_tf is None else round(100 * bwd_tf / peak, 2),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": None if bwd_ms is None else round(bwd_ms, 4),
+        "fwd_tflops": res["fwd_tflops"],
+        "fwd_pct_of_peak": res["fwd_pct_of_peak"],
+        "bwd_tflops": res.get("bwd_tflops"),
+        "bwd_pct_of_peak": res.get("bwd_pct_of_peak"),
+        "fwd_ms": res["fwd_ms"],
+        "bwd_ms": res.get("bwd_ms"),
+        "step_group_ms": res["step_group_ms"],
+        "fwd_group_ms": res["fwd_group_ms"],
         "kernel_ms_note": "per-kernel spans from a second pass of the same steps with an event "
                           "between kernels (about 12 us of event cost per kernel boundary)",
         "wall_s_timed_region": round(wall, 4),
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
+        "clocks": {"before": clocks_before, "sclk_mhz_during_timed_steps": during[0],
+                   "after": clocks_after,
+                   "note": "before/after are read with the GPU idle; the sample during the "
+                           "timed steps is taken once they are all enqueued; the effective "
+                           "clock per kernel (GRBM_GUI_ACTIVE over kernel time) is in the "
+                           "counter summaries"},
         "roofline": roofline,
     }
+    if not args.no_extra and args.workload == "gqa_causal":
+        del run
+        torch.cuda.empty_cache()
+        line["workloads"] = extra_workloads(dev, stream, max(args.steps // 2, 6), args.warmup)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
