@@ -513,9 +513,10 @@ def roofline_fracs(w, res, peak):
 # Workloads measured beside the default one in the same run: the DiT
 # self-attention forward (its own >= 50% gate), the two DiT cross-attention
 # shapes and the decoder shape against their rooflines, warm and with inputs
-# rotated through more memory than the 256 MB last-level cache.
+# rotated through more memory than the 256 MB last-level cache, and the
+# float32 path (against the fp32 matrix peak).
 EXTRA = [("dit_self", False), ("dit_cross_512", True), ("dit_cross_257", True),
-         ("decoder_mha_causal", True)]
+         ("decoder_mha_causal", True), ("vae_attn_f32", False)]
 ROTATE_BYTES = 1 << 30
 
 

@@ -72,6 +72,14 @@ WORKLOADS: Dict[str, Workload] = {
                  qk_mult=1.0 / math.sqrt(2.0)),
         Workload("dit_cross_512", 1, 10, 10, 32760, 512, 128, False, "bf16", 51, True),
         Workload("dit_cross_257", 1, 10, 10, 32760, 257, 128, False, "bf16", 52, True),
+        # float32 attention over the latent frames of one generated chunk of a
+        # 480x832 video, the VAE's fp32 attention that the LingBot report's
+        # kernel ledger names without printing its shape: each frame attends
+        # over its own 60x104 tokens (before the 2x2 patches that give the
+        # report's 30x52 DiT tokens per frame), a chunk is 3 latent frames
+        # (the report's per-chunk 4680 = 3 x 1560 tokens) taken as the batch,
+        # and the channel width is taken as 3 heads of 128.
+        Workload("vae_attn_f32", 3, 3, 3, 6240, 6240, 128, False, "f32", 71, True),
     ]
 }
 

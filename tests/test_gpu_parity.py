@@ -60,9 +60,28 @@ def test_parity_tiny_f32_workload(dev):
     H.check_full(W.WORKLOADS["tiny_mha_f32"], dev)
 
 
-# The five workloads at full size, every element.
+# The float32 path on the fp32 matrix cores, at shapes that take each of its
+# workgroup sizes (4, 2 and 1 waves of 32 rows or keys; f32_waves in
+# attn_f32.hip picks them from the row or key count), with ragged tails,
+# grouped heads, bottom-right causal masking and a short, tile-misaligned key
+# range.  Forward and dQ / dK-dV waves per workgroup: 4/4, 4/2, 2/1, 1/1, 1/1.
+F32 = [
+    wl("f32_w4_noncausal_d64", 2, 8, 8, 4100, 4200, 64, False, dtype="f32"),
+    wl("f32_w4_w2_causal_gqa_d128", 1, 4, 2, 8200, 8200, 128, True, dtype="f32"),
+    wl("f32_w2_w1_causal_gqa_d128", 1, 4, 2, 6000, 6000, 128, True, dtype="f32"),
+    wl("f32_bottom_right_d128", 1, 3, 1, 77, 301, 128, True, dtype="f32"),
+    wl("f32_cross_257_d128", 1, 4, 4, 2000, 257, 128, False, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("w", F32, ids=[w.name for w in F32])
+def test_parity_f32_matrix_path(w, dev):
+    H.check_full(w, dev)
+
+
+# The five workloads (and the float32 VAE-frame one) at full size, every element.
 @pytest.mark.parametrize("name", ["decoder_mha_causal", "gqa_causal", "dit_self", "dit_cross_512",
-                                  "dit_cross_257"])
+                                  "dit_cross_257", "vae_attn_f32"])
 def test_parity_workload_full(name, dev):
     w = W.WORKLOADS[name]
     H.check_full(w, dev, backward=w.backward)
