@@ -310,30 +310,20 @@ def main_paged(args, w):
 
 
 def read_clocks():
-    """Current GPU clocks: sclk from torch (amdsmi), sclk and mclk as rocm-smi
-    reports them.  Either may be None where the tool is unavailable."""
-    import subprocess
-
-    import torch
-
-    out = {"sclk_mhz": None, "rocm_smi": None}
+    """Current GPU clocks in MHz (sclk and mclk), read in-process through
+    amdsmi: no child program may be started once the GPU is initialised.
+    Either may be None where the interface is unavailable."""
+    out = {"sclk_mhz": None, "mclk_mhz": None}
     try:
-        out["sclk_mhz"] = int(torch.cuda.clock_rate(0))
-    except Exception:  # pragma: no cover - tool missing
-        pass
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
-                           timeout=20)
-        data = json.loads(r.stdout)
-        card = {}
-        for _, vals in sorted(data.items()):
-            for key, val in vals.items():
-                k = key.lower()
-                if k.startswith(("sclk", "mclk", "fclk")):
-                    card[key.strip(" :")] = val
-            break
-        out["rocm_smi"] = card or None
-    except Exception:  # pragma: no cover
+        import amdsmi
+        import torch
+
+        handle = torch.cuda._get_amdsmi_handler(torch.device("cuda:0"))
+        for key, typ in (("sclk_mhz", amdsmi.AmdSmiClkType.GFX), ("mclk_mhz", amdsmi.AmdSmiClkType.MEM)):
+            info = amdsmi.amdsmi_get_clock_info(handle, typ)
+            val = info.get("cur_clk", info.get("clk"))
+            out[key] = int(val) if isinstance(val, (int, float)) else None
+    except Exception:  # pragma: no cover - interface missing
         pass
     return out
 
@@ -661,10 +651,10 @@ def main():
         "kernel_ms": {n: round(t, 4) for n, t in kern_ms.items()},
         "clocks": {"before": clocks_before, "sclk_mhz_during_timed_steps": during[0],
                    "after": clocks_after,
-                   "note": "before/after are read with the GPU idle; the sample during the "
-                           "timed steps is taken once they are all enqueued; the effective "
-                           "clock per kernel (GRBM_GUI_ACTIVE over kernel time) is in the "
-                           "counter summaries"},
+                   "note": "amdsmi samples; before/after are read with the GPU idle, the "
+                           "sample during the timed steps once they are all enqueued; the "
+                           "effective clock per kernel (GRBM_GUI_ACTIVE over kernel time) is "
+                           "in the counter summaries"},
         "roofline": roofline,
     }
     if not args.no_extra and args.workload == "gqa_causal":
