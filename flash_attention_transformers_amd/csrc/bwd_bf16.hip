@@ -45,17 +45,29 @@
 
 namespace mattn {
 
+// Split count for the dK/dV walk.  One dK/dV workgroup fills a CU (its
+// LDS), and MI355X has 256 CUs, so the grid runs in rounds of 256
+// workgroups; a chunk of n_qt / ns query tiles is a workgroup's walk.  The
+// split minimises rounds x walk length, plus a charge of about a third of a
+// step per split for the partials' reduction, with at most 512 workgroups
+// (which bounds the partials to 64 MiB at D = 128) and at least 8 query
+// tiles per chunk.  Depends only on the sizes.
 int bwd_nsplit(int B, int Hkv, int Sq, int Skv) {
   if (B <= 0 || Hkv <= 0 || Sq <= 0 || Skv <= 0) return 1;
+  constexpr long long kSlots = 256, kMaxWgs = 2 * kSlots;
   const long long n_kt = (Skv + BWD_BN - 1) / BWD_BN;
   const long long wgs = (long long)B * Hkv * n_kt;
-  const long long target = 512;
-  if (wgs >= target) return 1;
+  if (wgs >= kMaxWgs) return 1;
   const long long n_qt = (Sq + BWD_BMQ - 1) / BWD_BMQ;
-  long long ns = (target + wgs - 1) / wgs;
   const long long cap = n_qt / 8;  // keep at least 8 query tiles per chunk
-  if (ns > cap) ns = cap;
-  return ns < 1 ? 1 : (int)ns;
+  auto cost = [&](long long ns) {   // in tenths of a step
+    const long long rounds = (wgs * ns + kSlots - 1) / kSlots;
+    return 10 * rounds * ((n_qt + ns - 1) / ns) + 3 * ns;
+  };
+  long long best = 1;
+  for (long long ns = 2; ns <= cap && wgs * ns <= kMaxWgs; ++ns)
+    if (cost(ns) < cost(best)) best = ns;
+  return (int)best;
 }
 
 namespace {

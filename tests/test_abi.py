@@ -328,11 +328,11 @@ def test_noalloc_rejects_unsupported():
 
 
 def test_noalloc_rejects_problems_beyond_the_scratch():
-    # Dlt of 3 * 5592405 rows (64 MiB) plus split partials exceeds the 128 MiB array.
-    B, Hq, Hkv, Sq, Skv, D = 1, 3, 3, 5592405, 100, 128
+    # Dlt of 2^25 - 1 rows (128 MiB) plus split partials exceeds the 128 MiB array.
+    B, Hq, Hkv, Sq, Skv, D = 1, 1, 1, (1 << 25) - 1, 100, 64
     assert fa.mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D) > fa.MATTN_SCRATCH_BYTES
     assert noalloc_status(B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, Skv=Skv, D=D) == fa.MATTN_ERR_SCRATCH
-    # the largest backward workspace among the workloads (DiT cross, 257 keys) fits
+    # the largest backward workspace among the workloads (DiT cross) fits
     assert fa.mattn_bwd_workspace_size(1, 10, 10, 32760, 257, 128) < fa.MATTN_SCRATCH_BYTES
     assert "scratch" in fa.mattn_strerror(fa.MATTN_ERR_SCRATCH)
 

@@ -71,8 +71,8 @@ def test_noalloc_rejects_a_problem_beyond_the_scratch(dev):
     import torch
 
     lib = fa.load_library()
-    # Dlt of 3 * 5592405 rows (64 MiB) plus split partials: just over 128 MiB.
-    B, Hq, Hkv, Sq, Skv, D = 1, 3, 3, 5592405, 100, 128
+    # Dlt of 2^25 - 1 rows (128 MiB) plus split partials: over 128 MiB.
+    B, Hq, Hkv, Sq, Skv, D = 1, 1, 1, (1 << 25) - 1, 100, 64
     assert fa.mattn_bwd_workspace_size(B, Hq, Hkv, Sq, Skv, D) > fa.MATTN_SCRATCH_BYTES
     x = torch.full((64,), float("nan"), device=dev)
     p = ctypes.c_void_p(x.data_ptr())  # never dereferenced: the call is rejected first
