@@ -386,6 +386,8 @@ class DenseRun:
         base = W.to_torch(inp, dev)
         del inp
         self.sets = []
+        # One workspace serves every copy: each step rewrites what it reads.
+        ws = fa.bwd_workspace(base["q"], base["k"]) if w.backward else None
         for r in range(copies):
             t = {n: (x if r == 0 else x.clone()) for n, x in base.items()}
             t["o"] = torch.empty_like(t["q"])
@@ -393,7 +395,7 @@ class DenseRun:
             if w.backward:
                 t["dq"], t["dk"], t["dv"] = (torch.empty_like(t["q"]), torch.empty_like(t["k"]),
                                              torch.empty_like(t["v"]))
-                t["ws"] = fa.bwd_workspace(t["q"], t["k"])
+                t["ws"] = ws
             self.sets.append(t)
         # The stages mattn_bwd enqueues: bf16 forms D inside the dQ kernel.
         if not w.backward:
@@ -405,7 +407,8 @@ class DenseRun:
             self.names = ["fwd", "pre", "dq", "dkdv"]
 
     def footprint(self) -> int:
-        return sum(x.numel() * x.element_size() for x in self.sets[0].values())
+        """Bytes of one copy of the inputs and outputs (the shared workspace aside)."""
+        return sum(x.numel() * x.element_size() for n, x in self.sets[0].items() if n != "ws")
 
     def fwd(self, i: int):
         t, w = self.sets[i % len(self.sets)], self.w

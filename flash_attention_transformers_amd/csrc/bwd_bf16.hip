@@ -213,7 +213,7 @@ struct DkdvCopy<128> {
 // query head of the group; tile it arrives by direct copies two steps ahead
 // into buffer it % 3 (each buffer its own LDS object, so reads never wait for
 // copies in flight to the others).  One barrier per step:
-//   P-wave : S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e) -> P (bf16) to LDS
+//   P-wave : S = Q K^T, P = 2^(S*scale*log2e - LSE*log2e) -> P (fp16) to LDS
 //            | barrier |  dV^T += dO^T P
 //   dS-wave: dK^T += Q(it-1)^T dS(it-1), dP = dO V^T
 //            | barrier |  dS = P (dP - Dlt)
@@ -234,9 +234,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
   __shared__ __attribute__((aligned(16))) char QT0[Copy::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) char QT1[Copy::BUF_BYTES];
   __shared__ __attribute__((aligned(16))) char QT2[Copy::BUF_BYTES];
-  // P handed from each P-wave to its dS-wave, by step parity:
-  // [parity][slice][sub-block][half][lane][8 bf16] (16 bytes per lane, so
-  // a wave's 16-byte accesses cover all banks once).
+  // P handed from each P-wave to its dS-wave, by step parity, as fp16:
+  // [parity][slice][sub-block][half][lane][8 fp16] (16 bytes per lane, so
+  // a wave's 16-byte accesses cover all banks once).  fp16 rather than bf16:
+  // the same bytes with three more mantissa bits, and the dS-wave multiplies
+  // it in without widening it first (v_fma_mix_f32).
   constexpr int PEX_PAR = 4 * NSUB * 64 * 16;
   __shared__ __attribute__((aligned(16))) bf16 Pex[2 * PEX_PAR];
   auto QTbuf = [&](auto b) __attribute__((always_inline)) -> char* {
@@ -354,9 +356,12 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
   };
-  // P = 2^(S*c - LSE*log2e), masked above the causal diagonal; P (bf16)
-  // stays in registers for dV and goes to the dS-wave through LDS.
+  // P = 2^(S*c - LSE*log2e), masked above the causal diagonal; P rounded to
+  // bf16 stays in registers for dV, and P rounded to fp16 (nearest even; P
+  // lies in [0, 1]) goes to the dS-wave through LDS.
   bf16x8 pb[NSUB][2];
+  u32x4 ph[NSUB][2];  // the same P as fp16 pairs, for the dS-wave
+  float pr_keep[4];
   auto exp_tile = [&](auto masked, const float* lse, bf16* pex, int qt0,
                       const f32x16 (&sc)[NSUB]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(masked)::value;
@@ -373,11 +378,14 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           const int i = 4 * blk + j;
           float pr = fast_exp2(__builtin_fmaf(sc[qb][i], c, -Lv[j] * MATTN_LOG2E));
           if (MASK && y > 8 * blk + j) pr = 0.f;
+          pr_keep[j] = pr;
           pb[qb][i >> 3][i & 7] = (bf16)pr;
         }
+        ph[qb][blk >> 1][(blk & 1) * 2] = pack_f16x2(pr_keep[0], pr_keep[1]);
+        ph[qb][blk >> 1][(blk & 1) * 2 + 1] = pack_f16x2(pr_keep[2], pr_keep[3]);
       }
-      *reinterpret_cast<bf16x8*>(pex + (2 * qb) * 64 * 8) = pb[qb][0];
-      *reinterpret_cast<bf16x8*>(pex + (2 * qb + 1) * 64 * 8) = pb[qb][1];
+      *reinterpret_cast<u32x4*>(pex + (2 * qb) * 64 * 8) = ph[qb][0];
+      *reinterpret_cast<u32x4*>(pex + (2 * qb + 1) * 64 * 8) = ph[qb][1];
     }
   };
   // dV^T += dO^T P.
@@ -402,21 +410,24 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
-  // dS = P (dP - Dlt), rounded to bf16 as the B operand of dK^T += Q^T dS.
+  // dS = P (dP - Dlt) from the fp16 P, rounded to bf16 as the B operand of
+  // dK^T += Q^T dS.
   auto ds_tile = [&](const float* dlt, const bf16* pex, const f32x16 (&dp)[NSUB],
                      bf16x8 (&dsb)[NSUB][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int qb = 0; qb < NSUB; ++qb) {
-      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(pex + (2 * qb) * 64 * 8);
-      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(pex + (2 * qb + 1) * 64 * 8);
+      const f16x8 p0 = *reinterpret_cast<const f16x8*>(pex + (2 * qb) * 64 * 8);
+      const f16x8 p1 = *reinterpret_cast<const f16x8*>(pex + (2 * qb + 1) * 64 * 8);
 #pragma unroll
       for (int blk = 0; blk < 4; ++blk) {
         const f32x4 Dl = *reinterpret_cast<const f32x4*>(&dlt[qb * 32 + 8 * blk + 4 * g]);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = 4 * blk + j;
-          const float pv = (float)(i < 8 ? p0[i] : p1[i - 8]);
-          dsb[qb][i >> 3][i & 7] = (bf16)(pv * (dp[qb][i] - Dl[j]));
+          // fp16 P times an fp32 difference: one mixed-precision FMA
+          // (v_fma_mix_f32), with no separate widening of P.
+          const _Float16 ph16 = i < 8 ? p0[i] : p1[i - 8];
+          dsb[qb][i >> 3][i & 7] = (bf16)__builtin_fmaf((float)ph16, dp[qb][i] - Dl[j], 0.f);
         }
       }
     }

@@ -21,6 +21,8 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 #define MATTN_INF __builtin_huge_valf()
 #define MATTN_LOG2E 1.4426950408889634f
@@ -339,6 +341,11 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   bf16 x = (bf16)a, y = (bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
+
+// Two floats as fp16, rounded to nearest even (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, f16x2{(_Float16)a, (_Float16)b});
 }
 
 // Bytes of LDS that store_rows_bf16 stages one wave's 32 rows in.
