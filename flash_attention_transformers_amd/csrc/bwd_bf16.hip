@@ -724,6 +724,22 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     dhalf = dlt_half_row_step(dof[s], as_bf16x8(obuf.ld16((uint32_t)(qrow * D + 16 * s + 8 * g) * 2)), dhalf);
   const float dl = dhalf + __shfl_xor(dhalf, 32);
   if (g == 0 && qrow < Sq) DLT[(size_t)bh * Sq + qrow] = dl;
+  // dP^T - Dlt straight from the matrix unit: each dP^T accumulator starts
+  // from one MFMA of a ones operand (k = 0..2 on the g = 0 lanes, zero
+  // elsewhere) with this lane's -Dlt as three bf16 terms that sum to it
+  // exactly (each the top bits of what the previous ones leave).
+  bf16x8 ones_a, ndl_b;
+  {
+    const u32x4 o = g == 0 ? u32x4{0x3f803f80u, 0x3f80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u};
+    const float x = -dl;
+    const uint32_t hi = __builtin_bit_cast(uint32_t, x) & 0xffff0000u;
+    const float r1 = x - __builtin_bit_cast(float, hi);
+    const uint32_t mid = __builtin_bit_cast(uint32_t, r1) & 0xffff0000u;
+    const float r2 = r1 - __builtin_bit_cast(float, mid);
+    const u32x4 t = {(hi >> 16) | mid, __builtin_bit_cast(uint32_t, r2) >> 16, 0u, 0u};
+    ones_a = __builtin_bit_cast(bf16x8, o);
+    ndl_b = __builtin_bit_cast(bf16x8, t);
+  }
 
   f32x16 adq[D / 32];  // dQ^T of this wave's 32 rows
 #pragma unroll
@@ -741,7 +757,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     const int j0 = kt * DQ_BN;
     auto step = [&](auto masked, int kb0) __attribute__((always_inline)) {
       constexpr bool MASK = decltype(masked)::value;
-      f32x16 s = zero_f32x16(), dp = zero_f32x16();
+      f32x16 s = zero_f32x16(), dp = mfma32(ones_a, ndl_b, zero_f32x16());
 #pragma unroll
       for (int st0 = 0; st0 < D / 16; st0 += 4) {
         bf16x8 ak[4], av[4];
@@ -764,7 +780,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
           const int kk = j0 + kb0 + crow(i, g);
           if (kk >= Skv || (CAUSAL && kk > qrow + diag)) p = 0.f;
         }
-        dsb[i >> 3][i & 7] = (bf16)(p * (dp[i] - dl));
+        dsb[i >> 3][i & 7] = (bf16)(p * dp[i]);
       }
       // dQ^T += K^T dS^T over this wave's 32 keys.
 #pragma unroll
