@@ -773,13 +773,17 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
         }
       }
       bf16x8 dsb[2];
+      // Key j0 + kb0 + crow(i, g) is visible iff crow(i, 0) <= lim.
+      int lim = 0;
+      if (MASK) {
+        int last = Skv - 1;
+        if (CAUSAL) last = min(last, qrow + diag);
+        lim = last - j0 - kb0 - 4 * g;
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float p = fast_exp2(__builtin_fmaf(s[i], c, -lse2));
-        if (MASK) {
-          const int kk = j0 + kb0 + crow(i, g);
-          if (kk >= Skv || (CAUSAL && kk > qrow + diag)) p = 0.f;
-        }
+        if (MASK && crow(i, 0) > lim) p = 0.f;
         dsb[i >> 3][i & 7] = (bf16)(p * dp[i]);
       }
       // dQ^T += K^T dS^T over this wave's 32 keys.

@@ -204,13 +204,18 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
     return mx;
   };
   auto max_masked = [&](f32x16 (&sc)[KB], int t, int qrow) {
+    // Key t*BN + 32 kb + crow(i, g) is visible iff it is at most the last
+    // visible key, i.e. iff crow(i, 0) <= lim - 32 kb: one compare with a
+    // constant per element.
+    int last = Skv - 1;
+    if (CAUSAL) last = min(last, qrow + diag);
+    const int lim = last - t * FWD_BN - 4 * g;
     float mx = -MATTN_INF;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = t * FWD_BN + kb * 32 + crow(i, g);
-        const bool ok = key < Skv && (!CAUSAL || key <= qrow + diag);
+        const bool ok = crow(i, 0) <= lim - 32 * kb;
         sc[kb][i] = ok ? sc[kb][i] : -MATTN_INF;
         mx = fmaxf(mx, sc[kb][i]);
       }
