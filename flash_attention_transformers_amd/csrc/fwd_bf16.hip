@@ -290,18 +290,20 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K,
 #pragma unroll
       for (int i = 0; i < 4; ++i) rs[qb][i] = 0.f;
     // Phase 1: the MFMAs of S(t+1) with the 112 VALU instructions per query
-    // block that turn S(t) into P(t).
+    // block that turn S(t) into P(t): five after each MFMA, the rest after
+    // the last (measured 1-3% faster than spreading them evenly), with the
+    // K operand reads eight MFMAs ahead.
     s_tile(Ks(p1), nxt);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) exp_block(cur[qb][kb], qb, kb, rs[qb]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    for (int i = 0; i < 8; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
     for (int i = 0; i < NMF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
