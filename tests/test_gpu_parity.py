@@ -105,6 +105,22 @@ def test_parity_eight_wave_forward(w, dev):
     H.check_full(w, dev, backward=False)
 
 
+# Short key sequences at D = 128 under many query rows, forward only: grouped
+# KV heads with a ragged last query tile, one key tile (64 keys), a single
+# key (a walk of one tile whose softmax is exactly 1) and eight full tiles.
+SHORT_KV = [
+    wl("short_kv_gqa4_ragged_300", 1, 32, 8, 2100, 300, 128, False, backward=False),
+    wl("short_kv_one_tile_64", 2, 16, 16, 2000, 64, 128, False, backward=False),
+    wl("short_kv_single_key", 1, 64, 64, 1030, 1, 128, False, backward=False),
+    wl("short_kv_eight_tiles_512", 4, 8, 2, 2048, 512, 128, False, backward=False),
+]
+
+
+@pytest.mark.parametrize("w", SHORT_KV, ids=[w.name for w in SHORT_KV])
+def test_parity_short_kv_forward(w, dev):
+    H.check_full(w, dev, backward=False)
+
+
 # Backward on a long GQA shape (group size 2) with ragged lengths and the
 # causal diagonal off the tile grid.
 def test_parity_long_gqa_backward(dev):
