@@ -121,6 +121,24 @@ def test_parity_short_kv_forward(w, dev):
     H.check_full(w, dev, backward=False)
 
 
+# Large query groups: multi-query attention (group of 16 on one KV head,
+# causal), a group of 8 at D = 64 with ragged lengths, a group of 8 large
+# enough for the eight-wave four-head forward (two workgroups per KV head)
+# with its backward, and a group of 16 on the split short-KV backward.  The
+# dK/dV kernel sums each KV head's whole group in registers.
+GROUPS = [
+    wl("mqa_g16_causal", 1, 16, 1, 300, 300, 128, True),
+    wl("g8_d64_ragged", 2, 16, 2, 200, 457, 64, False),
+    wl("g8_w8_head_quads_causal", 1, 32, 4, 4100, 4100, 128, True),
+    wl("g16_split_short_kv", 1, 16, 1, 1500, 200, 128, False),
+]
+
+
+@pytest.mark.parametrize("w", GROUPS, ids=[w.name for w in GROUPS])
+def test_parity_large_groups(w, dev):
+    H.check_full(w, dev, backward=w.backward)
+
+
 # Backward on a long GQA shape (group size 2) with ragged lengths and the
 # causal diagonal off the tile grid.
 def test_parity_long_gqa_backward(dev):
