@@ -210,6 +210,72 @@ def test_negative_and_zero_scale(shape, dev):
                 assert np.abs(H.to_np(g["dq"])).max() == 0 and np.abs(H.to_np(g["dk"])).max() == 0
 
 
+def _bwd_noalloc(lib, t, o, lse, dq, dk, dv, w, stream):
+    import ctypes
+
+    vp = ctypes.c_void_p
+    return lib.mattn_bwd_noalloc(
+        vp(t["q"].data_ptr()), vp(t["k"].data_ptr()), vp(t["v"].data_ptr()), vp(o.data_ptr()),
+        vp(lse.data_ptr()), vp(t["do"].data_ptr()), vp(dq.data_ptr()), vp(dk.data_ptr()),
+        vp(dv.data_ptr()), w.B, w.Hq, w.Hkv, w.Sq, w.Skv, w.D, int(w.causal),
+        ctypes.c_float(w.scale), 0, vp(stream))
+
+
+@pytest.mark.parametrize("shape", [(1, 8, 2, 700, 700, 128, True), (1, 4, 4, 1500, 257, 128, False)])
+def test_graph_capture_replays(shape, dev):
+    """mattn_fwd and mattn_bwd_noalloc captured into one HIP graph (torch's
+    graph API; every tensor allocated beforehand; the calls enqueue kernels
+    only), then replayed on three input sets that eager copies place in the
+    captured buffers, with synchronisations between the replays: every
+    replay gives the bits of eager mattn_fwd / mattn_bwd on the same inputs.
+    The second shape takes the split short-KV backward (fp32 partials in the
+    static scratch and their fixed-order reduction)."""
+    import torch
+
+    B, Hq, Hkv, Sq, Skv, D, causal = shape
+    H.say(f"[graph] {shape}")
+    wls = [W.Workload("graph", B, Hq, Hkv, Sq, Skv, D, causal, "bf16", s, True) for s in (31, 32, 33)]
+    ins = [W.to_torch(W.make_inputs(w), dev) for w in wls]
+    w = wls[0]
+    static = {n: ins[0][n].clone() for n in ("q", "k", "v", "do")}
+    o = torch.empty_like(static["q"])
+    lse = torch.empty(B, Hq, Sq, dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(static[n]) for n in ("q", "k", "v"))
+    lib = fa.load_library()
+
+    def run(stream):
+        fa.mattn_fwd(static["q"], static["k"], static["v"], o, lse, causal=causal, scale=w.scale,
+                     stream=stream)
+        assert _bwd_noalloc(lib, static, o, lse, dq, dk, dv, w, stream.cuda_stream) == 0
+
+    # Eager warm-up on a side stream; it also looks up the scratch array's
+    # device address, so the capture itself makes no runtime queries of that.
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        run(side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    for rep, t in enumerate(ins):
+        for n in static:
+            static[n].copy_(t[n])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = fwd_bwd(t, causal, scale=w.scale)
+        torch.cuda.synchronize()
+        got = dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv)
+        for n in ref:
+            a, b = got[n], ref[n]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), f"replay {rep}: {n}"
+
+
 @pytest.mark.parametrize("shape", [(1, 8, 2, 300, 300, 128, True), (1, 2, 2, 1000, 257, 128, False),
                                    (1, 2, 2, 100, 70, 64, False)])
 def test_stage_sequence_equals_bwd(shape, dev):
