@@ -276,6 +276,43 @@ def test_graph_capture_replays(shape, dev):
             assert torch.equal(a, b), f"replay {rep}: {n}"
 
 
+def test_concurrent_streams(dev):
+    """Forward and backward of two problems enqueued on two streams at once,
+    each with its own workspace, give the same bits as the same calls made
+    one after the other: the library keeps no state shared between calls
+    (the allocation-free backward's static scratch aside)."""
+    import torch
+
+    H.say("[two streams]")
+    shapes = [(1, 8, 2, 900, 900, 128, True), (1, 4, 4, 1500, 257, 128, False)]
+    wls = [W.Workload("streams", *s, "bf16", 61 + i, True) for i, s in enumerate(shapes)]
+    ins = [W.to_torch(W.make_inputs(w), dev) for w in wls]
+    ref = [fwd_bwd(t, w.causal, scale=w.scale) for t, w in zip(ins, wls)]
+    torch.cuda.synchronize()
+    outs = []
+    for t in ins:
+        o = torch.empty_like(t["q"])
+        lse = torch.empty(t["q"].shape[:3], dtype=torch.float32, device=dev)
+        outs.append(dict(o=o, lse=lse, dq=torch.empty_like(t["q"]), dk=torch.empty_like(t["k"]),
+                         dv=torch.empty_like(t["v"]), ws=fa.bwd_workspace(t["q"], t["k"])))
+    streams = [torch.cuda.Stream(device=dev) for _ in ins]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream(dev))
+    for t, w, g, s in zip(ins, wls, outs, streams):
+        fa.mattn_fwd(t["q"], t["k"], t["v"], g["o"], g["lse"], causal=w.causal, scale=w.scale,
+                     stream=s)
+    for t, w, g, s in zip(ins, wls, outs, streams):
+        fa.mattn_bwd(t["q"], t["k"], t["v"], g["o"], g["lse"], t["do"], g["dq"], g["dk"], g["dv"],
+                     g["ws"], causal=w.causal, scale=w.scale, stream=s)
+    torch.cuda.synchronize()
+    for i, (g, r) in enumerate(zip(outs, ref)):
+        for n in r:
+            a, b = g[n], r[n]
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b), f"problem {i}: {n}"
+
+
 @pytest.mark.parametrize("shape", [(1, 8, 2, 300, 300, 128, True), (1, 2, 2, 1000, 257, 128, False),
                                    (1, 2, 2, 100, 70, 64, False)])
 def test_stage_sequence_equals_bwd(shape, dev):
