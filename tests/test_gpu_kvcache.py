@@ -177,3 +177,51 @@ def test_bad_page_ids_and_lengths_do_not_fault(dev):
     ro, rl = oracle.kvcache_forward(v["q"][:1], v["k_cache"], v["v_cache"], inp.block_table[:1],
                                     [w.pages_per_seq * 64], True, w.scale)
     assert H.max_abs(H.to_np(o3[:1]), ro) <= TOL["o_max_abs"]
+
+
+def test_kvcache_graph_replay_follows_device_lengths(dev):
+    """mattn_fwd_kvcache captured into a HIP graph (every buffer allocated
+    beforehand, the split workspace sized from the shapes alone), then
+    replayed with new queries and new per-sequence lengths written into the
+    captured buffers between replays, as a decode loop does: each replay
+    gives the bits of an eager call on the same inputs, including a length
+    of 0 (a row with no key)."""
+    import torch
+
+    w = W.PagedWorkload("graph", 3, 8, 2, 1, 128, 64, (700, 64, 1500), True, seed=37)
+    H.say(f"[kvcache graph] {w}")
+    t = W.paged_to_torch(W.make_paged_inputs(w), dev)
+    q = t["q"].clone()
+    sl = t["seqlens"].clone()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    need = fa.mattn_fwd_kvcache_workspace_size(w.B, w.Hq, w.Hkv, w.Sq, w.D, w.page_size,
+                                               w.pages_per_seq)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+
+    def call(stream):
+        fa.mattn_fwd_kvcache(q, t["k_cache"], t["v_cache"], t["block_table"], sl, o, lse, ws,
+                             causal=True, scale=w.scale, stream=stream)
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        call(side)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(torch.cuda.current_stream(dev))
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=dev).manual_seed(5)
+    for rep, lens in enumerate([(700, 64, 1500), (701, 0, 1499), (1, 640, 1536)]):
+        q.copy_(torch.randn(q.shape, generator=gen, device=dev).to(q.dtype))
+        sl.copy_(torch.tensor(lens, dtype=torch.int32, device=dev))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ro, rl = fa.fwd_kvcache(q, t["k_cache"], t["v_cache"], t["block_table"], sl, causal=True,
+                                scale=w.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ro.view(torch.int16)), f"replay {rep}: o"
+        assert torch.equal(lse, rl), f"replay {rep}: lse"
